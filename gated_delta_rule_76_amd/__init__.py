@@ -1,0 +1,191 @@
+"""MI355X-native Kimi Delta Attention (KDA) forward: Python binding.
+
+Thin ctypes binding over ``libkda.so`` (the C ABI declared in include/kda.h).
+It only marshals arguments: every step of the computation runs in the HIP
+kernels.  PyTorch supplies device memory and the current stream.
+
+    o, S_T = kda_fwd_chunked(q, k, v, alpha, beta, S0, chunk=64)
+    o      = kda_decode_step(q, k, v, alpha, beta, S)   # S updated in place
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "KDA_F32", "KDA_BF16", "KdaError", "lib", "library_path", "exported_symbols",
+    "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
+    "status_string", "version",
+]
+
+KDA_F32 = 0
+KDA_BF16 = 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
+          3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
+# Every symbol include/kda.h declares.
+ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked",
+               "kda_fwd_chunked_workspace_bytes", "kda_decode_step")
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m gated_delta_rule_76_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.kda_version.argtypes = []
+        L.kda_version.restype = i
+        L.kda_status_string.argtypes = [i]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                      vp, sz, vp]
+        L.kda_fwd_chunked.restype = i
+        L.kda_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.kda_fwd_chunked_workspace_bytes.restype = sz
+        L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.kda_decode_step.restype = i
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> Tuple[str, ...]:
+    L = lib()
+    return tuple(s for s in ABI_SYMBOLS if hasattr(L, s))
+
+
+def version() -> int:
+    return int(lib().kda_version())
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------- raw calls
+def kda_fwd_chunked_raw(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
+                        workspace=None, workspace_bytes=0, stream=None) -> int:
+    """Direct C call with integer pointers (0/None for NULL); returns the status."""
+    return int(lib().kda_fwd_chunked(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v,
+                                     chunk, dtype, workspace, workspace_bytes, stream))
+
+
+def kda_decode_step_raw(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream=None) -> int:
+    return int(lib().kda_decode_step(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream))
+
+
+# ---------------------------------------------------------- torch front end
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"KDA tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
+                    return_state: bool = True):
+    """Chunked KDA prefill on the GPU.
+
+    q, k, alpha: [B,T,H,d_k]; v: [B,T,H,d_v]; beta: [B,T,H] (all bf16 or all
+    fp32, CUDA/HIP tensors); S0: [B,H,d_k,d_v] fp32 or None.  Returns (o, S_T);
+    S_T is None when return_state is False.  ``S_T`` may be S0 (in place).
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B,T,H,d_k]")
+    B, T, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    _dtype_code(q)
+    _check(k, "k", (B, T, H, d_k), dt, dev)
+    _check(alpha, "alpha", (B, T, H, d_k), dt, dev)
+    _check(v, "v", (B, T, H, d_v), dt, dev)
+    _check(beta, "beta", (B, T, H), dt, dev)
+    _check(q, "q", (B, T, H, d_k), dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", (B, T, H, d_v), dt, dev)
+    if return_state and S_T is None:
+        S_T = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _check(S_T, "S_T", (B, H, d_k, d_v), torch.float32, dev)
+    st = kda_fwd_chunked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+                             beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
+                             o.data_ptr(), S_T.data_ptr() if S_T is not None else None,
+                             B, T, H, d_k, d_v, chunk, _dtype_code(q), None, 0,
+                             _stream_handle(dev))
+    if st != 0:
+        raise KdaError(st, "kda_fwd_chunked")
+    return o, S_T
+
+
+def kda_decode_step(q, k, v, alpha, beta, S, *, o=None):
+    """One T=1 decode step; S [B,H,d_k,d_v] fp32 is updated in place.  Returns o."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d_k]")
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dt, dev = q.dtype, q.device
+    _dtype_code(q)
+    _check(k, "k", (B, H, d_k), dt, dev)
+    _check(alpha, "alpha", (B, H, d_k), dt, dev)
+    _check(v, "v", (B, H, d_v), dt, dev)
+    _check(beta, "beta", (B, H), dt, dev)
+    _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", (B, H, d_v), dt, dev)
+    st = kda_decode_step_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+                             beta.data_ptr(), S.data_ptr(), o.data_ptr(), B, H, d_k, d_v,
+                             _dtype_code(q), _stream_handle(dev))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step")
+    return o

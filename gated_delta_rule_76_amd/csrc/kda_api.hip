@@ -1,0 +1,105 @@
+// C ABI of the KDA library: argument validation and kernel dispatch.
+// The contract (layouts, ownership, errors) is documented in include/kda.h.
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;
+  return KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return kVersion; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_fwd_chunked_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
+                    int d_k, int d_v, int chunk, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  try {
+    if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (T > 0) {
+      if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+      if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
+          !aligned16(o))
+        return KDA_ERR_INVALID_ARG;
+      // beta is read one element at a time; natural alignment is enough
+      const uintptr_t esz = dtype == KDA_BF16 ? 2 : 4;
+      if (reinterpret_cast<uintptr_t>(beta) % esz != 0) return KDA_ERR_INVALID_ARG;
+    }
+    if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return KDA_ERR_INVALID_ARG;
+    if (workspace_bytes < kda_fwd_chunked_workspace_bytes(B, T, H, d_k, d_v, chunk, dtype))
+      return KDA_ERR_WORKSPACE;
+    (void)workspace;
+    // Token and state offsets are computed in 64-bit; keep grid sizes sane.
+    if (static_cast<long long>(B) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (!kda::prefill_supported(dtype == KDA_BF16, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+    if (T == 0 && S_T == nullptr) return KDA_OK;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.chunk = chunk;
+    a.bf16 = dtype == KDA_BF16;
+    a.stream = static_cast<hipStream_t>(stream);
+    return from_hip(kda::launch_prefill(a));
+  } catch (...) {
+    return KDA_ERR_HIP;
+  }
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
+                    int dtype, void* stream) {
+  try {
+    if (B < 1 || H < 1 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(S) ||
+        !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+    const uintptr_t esz = dtype == KDA_BF16 ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(beta) % esz != 0) return KDA_ERR_INVALID_ARG;
+    if (static_cast<long long>(B) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.S = S; a.o = o;
+    a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.bf16 = dtype == KDA_BF16;
+    a.stream = static_cast<hipStream_t>(stream);
+    return from_hip(kda::launch_decode(a));
+  } catch (...) {
+    return KDA_ERR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Host-side interface between the C ABI (kda_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  float* S;
+  void* o;
+  int B, H, d_k, d_v;
+  bool bf16;
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* S0;
+  void* o;
+  float* S_T;
+  int B, T, H, d_k, d_v, chunk;
+  bool bf16;
+  hipStream_t stream;
+};
+
+// Launch one decode step (validated arguments).
+hipError_t launch_decode(const DecodeArgs& a);
+
+// Launch the chunked prefill (validated arguments).  Returns
+// hipErrorNotSupported when no kernel is compiled for the size combination.
+hipError_t launch_prefill(const PrefillArgs& a);
+
+// Whether a prefill kernel exists for this combination (host-only check).
+bool prefill_supported(bool bf16, int d_k, int d_v, int chunk);
+
+}  // namespace kda

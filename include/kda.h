@@ -1,0 +1,128 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation (page "Yanjiu KimiK3, wo faxian damoxing zhengzai xuehui
+ * guanli ziji de jisuan", http://www.pwwt.cn/news/3763336/):
+ *
+ *   state        S_t in R^{d_k x d_v} per (batch, head)            (section 2.1)
+ *   update       S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+ *                      + beta_t k_t v_t^T,  alpha_t in [0,1]^{d_k}  (section 4)
+ *   readout      o_t = S_t^T q_t, taken after the update           (section 2.1)
+ *
+ * No query scaling and no key normalisation happen inside the library: q and
+ * k are used as given.  beta_t is one scalar per (token, head).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates or frees device memory and keeps no global
+ *     mutable state.
+ *   - Tensors are contiguous and row-major.  Pointers must be 16-byte aligned.
+ *   - `dtype` selects the element type of q, k, v, alpha, beta and o:
+ *     KDA_F32 (IEEE fp32) or KDA_BF16 (bfloat16).  The state is always fp32.
+ *     KDA_F32 computes in fp32 end to end; KDA_BF16 feeds bf16 operands to
+ *     the matrix cores with fp32 accumulation and an fp32 state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  Argument errors are
+ *     reported synchronously, before anything is launched; faults inside a
+ *     kernel surface when the caller synchronises the stream.
+ *   - Every call returns a kda_status (0 = success).  No C++ exception ever
+ *     crosses this boundary.
+ *   - Results are deterministic: the same inputs, sizes and stream give
+ *     bitwise identical outputs (no atomics, fixed reduction orders).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment, bad dtype */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not compiled: d_k, d_v, chunk combination */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    KDA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} kda_status;
+
+/* Library ABI version; bumped on any incompatible change. */
+KDA_API int kda_version(void);
+
+/* Human-readable name of a kda_status value (static storage, never NULL). */
+KDA_API const char *kda_status_string(int status);
+
+/*
+ * kda_fwd_chunked -- prefill: run the recurrence over T tokens for every
+ * (batch, head) chain, chunk by chunk.
+ *
+ * The sequence is cut into chunks of `chunk` tokens; the state is passed from
+ * chunk to chunk and each chunk's tokens are processed together through the
+ * compact "diagonal minus low rank" form of the chunk's transition product
+ * (section 6, chunking and the WY representation P = D - K W^T).  In exact
+ * arithmetic the result equals the token-by-token recurrence above.
+ *
+ *   q, k, alpha : [B, T, H, d_k]   dtype
+ *   v           : [B, T, H, d_v]   dtype
+ *   beta        : [B, T, H]        dtype
+ *   S0          : [B, H, d_k, d_v] fp32, or NULL for a zero initial state
+ *   o           : [B, T, H, d_v]   dtype, written (must not alias an input)
+ *   S_T         : [B, H, d_k, d_v] fp32, the state after token T-1, or NULL
+ *                 to skip it.  S_T may alias S0 (in-place update).
+ *   d_k, d_v    : each one of 16, 32, 64, 128
+ *   chunk       : one of 16, 32, 64 (KDA_F32 with d_k = 128 supports chunk
+ *                 <= 32: its fp32 chunk tiles would not fit in LDS)
+ *   workspace   : reserved; pass NULL and 0 (kda_fwd_chunked_workspace_bytes
+ *                 returns the size a configuration needs, currently 0)
+ *
+ * Semantics: T = 0 copies S0 (or zeros) to S_T and leaves o untouched.  A
+ * last chunk shorter than `chunk` is handled exactly (padding tokens write
+ * nothing and do not decay the state).
+ * Precondition of the chunked form: 0 < alpha <= 1 and, per channel, the
+ * product of alpha over any chunk stays above exp(-80) (fp32 range of the
+ * per-chunk decay factors).  Other gate values give unspecified results; the
+ * decode call below has no such restriction.
+ */
+KDA_API int kda_fwd_chunked(const void *q, const void *k, const void *v, const void *alpha,
+                    const void *beta, const float *S0, void *o, float *S_T,
+                    int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kda_fwd_chunked needs for these sizes (0 today). */
+KDA_API size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v,
+                                       int chunk, int dtype);
+
+/*
+ * kda_decode_step -- one token per sequence (T = 1), state updated in place.
+ *
+ * Per (b, h): S' = Diag(alpha) S; v_hat = S'^T k (the delta rule's
+ * prediction, section 3); u = beta (v - v_hat); S <- S' + k u^T; and
+ * o = S^T q, computed as S'^T q + (k^T q) u in the same single pass over S.
+ *
+ *   q, k, alpha : [B, H, d_k]      dtype
+ *   v           : [B, H, d_v]      dtype
+ *   beta        : [B, H]           dtype
+ *   S           : [B, H, d_k, d_v] fp32, read and overwritten in place
+ *   o           : [B, H, d_v]      dtype, written
+ *   d_k, d_v    : each one of 16, 32, 64, 128
+ *
+ * Exact for any alpha in [0,1], including alpha = 0.
+ */
+KDA_API int kda_decode_step(const void *q, const void *k, const void *v, const void *alpha,
+                    const void *beta, float *S, void *o, int B, int H, int d_k, int d_v,
+                    int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -16,11 +16,16 @@ distributions below are synthetic stand-ins:
 * alpha = exp(-softplus(N(0,1)) * c) per channel (c = 0.1 or 0.05);
 * S0 ~ 0.01 * N(0,1) in fp32 (or zero).
 
-Everything is drawn in float32 from numpy's PCG64 (seeded), normalised in
-float32, and, for bf16 workloads, rounded once to bf16 (round to nearest even)
+Everything is drawn in float32 from numpy's PCG64 and normalised in float32;
+for bf16 workloads it is then rounded once to bf16 (round to nearest even)
 while still stored as float32.  A float32 array that holds bf16-exact values
 converts to bf16 on the device without further rounding and to fp64 in the
 oracle exactly, so both sides see bit-identical inputs.
+
+Seeding: the flattened (batch, token, head) rows are cut into fixed blocks of
+32768 rows; block j of tensor i draws from PCG64(SeedSequence([seed, i, j])).
+Blocks are filled by a thread pool, and the bytes do not depend on the
+number of threads.
 
 Layouts (row-major, contiguous):
     q, k, alpha : [B, T, H, d_k]
@@ -54,27 +59,79 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     ties to even.  NaN stays NaN (quiet bit forced).
     """
     a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    r = r.astype(np.uint32)
+    u = a.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # wraps only for NaN patterns, fixed below
+    r &= np.uint32(0xFFFF0000)
     nan = np.isnan(a)
     if nan.any():
-        r[nan] = (a.view(np.uint32)[nan] | 0x00400000) & 0xFFFF0000
+        r[nan] = (u[nan] | np.uint32(0x00400000)) & np.uint32(0xFFFF0000)
     return r.view(np.float32).reshape(a.shape)
 
 
-def _l2_normalise(x: np.ndarray) -> np.ndarray:
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32))
-    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
+def _l2_normalise_(x: np.ndarray) -> None:
+    n = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))
+    x /= np.maximum(n, np.float32(1e-12))[..., None]
 
 
-def _softplus(x: np.ndarray) -> np.ndarray:
-    return np.logaddexp(np.float32(0.0), x).astype(np.float32)
+# Rows (token-heads) per independently seeded block.  Fixed, so the bytes
+# drawn do not depend on how many threads generate them.
+_BLOCK = 1 << 15
+_TENSORS = ("q", "k", "v", "alpha", "beta")
 
 
-def _sigmoid(x: np.ndarray) -> np.ndarray:
-    return (np.float32(1.0) / (np.float32(1.0) + np.exp(-x))).astype(np.float32)
+def _fill_block(out: dict, tid_seed: int, j: int, d_k: int, d_v: int, gate_c: float,
+                bf16: bool) -> None:
+    lo = j * _BLOCK
+    hi = min(lo + _BLOCK, out["q"].shape[0])
+    n = hi - lo
+    for ti, name in enumerate(_TENSORS):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([tid_seed, ti, j])))
+        if name in ("q", "k"):
+            x = rng.standard_normal((n, d_k), dtype=np.float32)
+            _l2_normalise_(x)
+        elif name == "v":
+            x = rng.standard_normal((n, d_v), dtype=np.float32)
+        elif name == "alpha":
+            x = rng.standard_normal((n, d_k), dtype=np.float32)
+            np.logaddexp(np.float32(0.0), x, out=x)          # softplus
+            x *= np.float32(-gate_c)
+            np.exp(x, out=x)                                  # exp(-c softplus)
+        else:
+            x = rng.standard_normal(n, dtype=np.float32)
+            np.negative(x, out=x)
+            np.exp(x, out=x)
+            x += np.float32(1.0)
+            np.reciprocal(x, out=x)                           # sigmoid
+        out[name][lo:hi] = round_to_bf16(x) if bf16 else x
+
+
+def _draw_token_tensors(seed: int, lead: tuple, d_k: int, d_v: int, gate_c: float,
+                        bf16: bool) -> dict:
+    import concurrent.futures as cf
+    import os
+
+    N = int(np.prod(lead)) if lead else 1
+    out = {"q": np.empty((N, d_k), np.float32), "k": np.empty((N, d_k), np.float32),
+           "v": np.empty((N, d_v), np.float32), "alpha": np.empty((N, d_k), np.float32),
+           "beta": np.empty((N,), np.float32)}
+    nblk = (N + _BLOCK - 1) // _BLOCK
+    workers = max(1, min(nblk, os.cpu_count() or 1, 16))
+    if workers == 1:
+        for j in range(nblk):
+            _fill_block(out, seed, j, d_k, d_v, gate_c, bf16)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda j: _fill_block(out, seed, j, d_k, d_v, gate_c, bf16), range(nblk)))
+    return {n: a.reshape(lead + a.shape[1:]) for n, a in out.items()}
+
+
+def _draw_state(seed: int, shape: tuple, std: float) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    x = rng.standard_normal(shape, dtype=np.float32)
+    x *= np.float32(std)
+    return x
 
 
 @dataclass(frozen=True)
@@ -120,21 +177,6 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def _draw_token_tensors(rng: np.random.Generator, lead: tuple, d_k: int, d_v: int,
-                        gate_c: float, bf16: bool):
-    q = _l2_normalise(rng.standard_normal(lead + (d_k,), dtype=np.float32))
-    k = _l2_normalise(rng.standard_normal(lead + (d_k,), dtype=np.float32))
-    v = rng.standard_normal(lead + (d_v,), dtype=np.float32)
-    xa = rng.standard_normal(lead + (d_k,), dtype=np.float32)
-    alpha = np.exp(-_softplus(xa) * np.float32(gate_c)).astype(np.float32)
-    del xa
-    beta = _sigmoid(rng.standard_normal(lead, dtype=np.float32))
-    out = dict(q=q, k=k, v=v, alpha=alpha, beta=beta)
-    if bf16:
-        out = {n: round_to_bf16(a) for n, a in out.items()}
-    return out
-
-
 def prefill_inputs(B: int, T: int, H: int, d_k: int, d_v: int, *, dtype: str = "bf16",
                    gate_c: float = 0.05, s0_std: float = 0.01, seed: int = 0) -> dict:
     """Draw one prefill batch.  Returns float32 numpy arrays (bf16-exact when
@@ -142,13 +184,8 @@ def prefill_inputs(B: int, T: int, H: int, d_k: int, d_v: int, *, dtype: str = "
     S0 [B,H,d_k,d_v] (None when s0_std == 0)."""
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
-    rng = np.random.Generator(np.random.PCG64(seed))
-    out = _draw_token_tensors(rng, (B, T, H), d_k, d_v, gate_c, dtype == "bf16")
-    if s0_std > 0:
-        out["S0"] = (rng.standard_normal((B, H, d_k, d_v), dtype=np.float32)
-                     * np.float32(s0_std)).astype(np.float32)
-    else:
-        out["S0"] = None
+    out = _draw_token_tensors(seed, (B, T, H), d_k, d_v, gate_c, dtype == "bf16")
+    out["S0"] = _draw_state(seed, (B, H, d_k, d_v), s0_std) if s0_std > 0 else None
     return out
 
 
@@ -168,10 +205,8 @@ def decode_pool(B: int, H: int, d_k: int, d_v: int, *, pool: int, dtype: str = "
     initial state S [B,H,d_k,d_v] fp32.  A run of N steps uses pool entry
     (step mod pool) at step `step`.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
-    out = _draw_token_tensors(rng, (pool, B, H), d_k, d_v, gate_c, dtype == "bf16")
-    out["S"] = (rng.standard_normal((B, H, d_k, d_v), dtype=np.float32)
-                * np.float32(s0_std)).astype(np.float32)
+    out = _draw_token_tensors(seed, (pool, B, H), d_k, d_v, gate_c, dtype == "bf16")
+    out["S"] = _draw_state(seed, (B, H, d_k, d_v), s0_std)
     return out
 
 

@@ -1,0 +1,103 @@
+"""The C ABI library loads and exports every symbol include/kda.h declares, and
+rejects bad arguments before launching anything (no GPU needed)."""
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_76_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    txt = open(os.path.join(ROOT, "include", "kda.h")).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_abi():
+    assert _header_symbols() == sorted(kda.ABI_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(kda.library_path())
+    assert sorted(kda.exported_symbols()) == _header_symbols()
+
+
+def test_version_and_status_strings():
+    assert kda.version() == 1
+    for code, name in kda.STATUS.items():
+        assert kda.status_string(code) == name
+    assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_query_is_zero():
+    assert kda.lib().kda_fwd_chunked_workspace_bytes(4, 16384, 16, 128, 128, 64, kda.KDA_BF16) == 0
+
+
+# Fake but 16-byte-aligned addresses: every call below must fail validation
+# before any launch, so nothing is ever dereferenced.
+P = 0x100000
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=None, o=P, S_T=P, B=1, T=64, H=1, d_k=64,
+             d_v=64, chunk=64, dtype=kda.KDA_BF16)
+    a.update(kw)
+    return kda.kda_fwd_chunked_raw(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], a["o"],
+                                   a["S_T"], a["B"], a["T"], a["H"], a["d_k"], a["d_v"], a["chunk"],
+                                   a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(alpha=None), 1),
+    (dict(beta=None), 1), (dict(o=None), 1),
+    (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1), (dict(dtype=7), 1),
+    (dict(q=P + 8), 1), (dict(o=P + 4), 1), (dict(S0=P + 4), 1), (dict(S_T=P + 2), 1),
+    (dict(beta=P + 1), 1),
+    (dict(d_k=48), 2), (dict(d_v=256), 2), (dict(chunk=128), 2), (dict(chunk=8), 2),
+    (dict(dtype=kda.KDA_F32, d_k=128, chunk=64), 2),
+])
+def test_fwd_validation(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_fwd_t0_without_state_is_a_no_op():
+    # T = 0 and no S_T: nothing to do, nothing launched, success.
+    assert _fwd(T=0, S_T=None, q=None, k=None, v=None, alpha=None, beta=None, o=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(S=P + 4), 1),
+    (dict(d_k=100), 2), (dict(dtype=3), 1),
+])
+def test_decode_validation(kw, code):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S=P, o=P, B=2, H=2, d_k=128, d_v=128,
+             dtype=kda.KDA_BF16)
+    a.update(kw)
+    assert kda.kda_decode_step_raw(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S"], a["o"],
+                                   a["B"], a["H"], a["d_k"], a["d_v"], a["dtype"]) == code
+
+
+def test_torch_front_end_checks_shapes():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.kda_fwd_chunked(q, q, q, q, torch.zeros(1, 4, 2), None)
+    with pytest.raises(TypeError):
+        kda.kda_fwd_chunked(q.double(), q.double(), q.double(), q.double(),
+                            torch.zeros(1, 4, 1, dtype=torch.float64), None)
+
+
+def test_package_never_imports_the_oracle():
+    import ast
+    pkg = os.path.join(ROOT, "gated_delta_rule_76_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith(".py"):
+                tree = ast.parse(open(os.path.join(dirpath, f)).read())
+                for node in ast.walk(tree):
+                    if isinstance(node, ast.Import):
+                        assert all(not a.name.startswith("oracle") for a in node.names), f
+                    if isinstance(node, ast.ImportFrom):
+                        assert not (node.module or "").startswith("oracle"), f

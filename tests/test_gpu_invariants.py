@@ -1,0 +1,204 @@
+"""GPU invariants of the chunked prefill and the decode step.
+
+Exact-in-exact-arithmetic properties, checked bitwise where the kernel does
+literally the same operations, and against the oracle's tolerance otherwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import orthonormal_key_set, prefill_inputs, round_to_bf16
+from tests.golden.load import overwrite_recall
+from tests.gpu_harness import TOL, log, rel_err, run_prefill, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import gated_delta_rule_76_amd as kda
+    return kda
+
+
+def _dev_inputs(x, dtype):
+    return [to_dev(x[n], dtype) for n in ("q", "k", "v", "alpha", "beta")]
+
+
+def test_determinism_bitwise():
+    log("[determinism] bf16 dk128 C64 B2 T300 H3, two runs")
+    x = prefill_inputs(2, 300, 3, 128, 128, dtype="bf16", seed=21)
+    o1, s1 = run_prefill(x, "bf16", 64)
+    o2, s2 = run_prefill(x, "bf16", 64)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 32)])
+def test_split_resume_aligned_is_bitwise(dtype, C):
+    import torch
+    kda = _kda()
+    log(f"[split/resume] {dtype} C{C}")
+    T1, T2 = 2 * C, 3 * C + 5
+    x = prefill_inputs(1, T1 + T2, 2, 128, 64, dtype=dtype, seed=22)
+    q, k, v, a, b = _dev_inputs(x, dtype)
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o_all, s_all = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C)
+    sl = lambda t, lo, hi: t[:, lo:hi].contiguous()
+    o1, s1 = kda.kda_fwd_chunked(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(a, 0, T1), sl(b, 0, T1), s0, chunk=C)
+    o2, s2 = kda.kda_fwd_chunked(sl(q, T1, None), sl(k, T1, None), sl(v, T1, None), sl(a, T1, None),
+                                 sl(b, T1, None), s1, chunk=C)
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[:, :T1], o1) and torch.equal(o_all[:, T1:], o2)
+    assert torch.equal(s_all, s2)
+
+
+def test_split_resume_ragged_within_tolerance():
+    import torch
+    kda = _kda()
+    log("[split/resume ragged] bf16 C64, split at 100")
+    x = prefill_inputs(1, 300, 2, 128, 128, dtype="bf16", seed=23)
+    q, k, v, a, b = _dev_inputs(x, "bf16")
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o_all, s_all = kda.kda_fwd_chunked(q, k, v, a, b, s0)
+    T1 = 100
+    sl = lambda t, lo, hi: t[:, lo:hi].contiguous()
+    o1, s1 = kda.kda_fwd_chunked(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(a, 0, T1), sl(b, 0, T1), s0)
+    o2, s2 = kda.kda_fwd_chunked(sl(q, T1, None), sl(k, T1, None), sl(v, T1, None), sl(a, T1, None),
+                                 sl(b, T1, None), s1)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    assert rel_err(to_np(torch.cat([o1, o2], dim=1)), o_ref) <= TOL["bf16"]
+    assert rel_err(to_np(s2), s_ref) <= TOL["bf16"]
+    assert rel_err(to_np(s2), to_np(s_all)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_steps_match_prefill(dtype):
+    import torch
+    kda = _kda()
+    log(f"[decode == prefill] {dtype} dk64 dv32 T40")
+    T = 40
+    x = prefill_inputs(2, T, 3, 64, 32, dtype=dtype, seed=24)
+    q, k, v, a, b = _dev_inputs(x, dtype)
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o_pre, s_pre = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=16)
+    S = s0.clone()
+    o_dec = torch.stack([kda.kda_decode_step(q[:, t].contiguous(), k[:, t].contiguous(),
+                                             v[:, t].contiguous(), a[:, t].contiguous(),
+                                             b[:, t].contiguous(), S) for t in range(T)], dim=1)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(o_dec), to_np(o_pre)) <= 2 * TOL[dtype]
+    assert rel_err(to_np(S), to_np(s_pre)) <= 2 * TOL[dtype]
+
+
+def test_t0_and_null_state():
+    import torch
+    kda = _kda()
+    log("[T=0 / S0=NULL / aliasing]")
+    x = prefill_inputs(2, 0, 3, 128, 128, dtype="bf16", seed=25)
+    q, k, v, a, b = _dev_inputs(x, "bf16")
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o = torch.full((2, 0, 3, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    _, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, o=o)
+    _, st0 = kda.kda_fwd_chunked(q, k, v, a, b, None)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0)
+    assert torch.count_nonzero(st0).item() == 0
+    # S0 = None equals an explicit zero state, bitwise
+    y = prefill_inputs(1, 150, 2, 128, 128, dtype="bf16", seed=26)
+    q, k, v, a, b = _dev_inputs(y, "bf16")
+    o1, s1 = kda.kda_fwd_chunked(q, k, v, a, b, None)
+    o2, s2 = kda.kda_fwd_chunked(q, k, v, a, b, torch.zeros(1, 2, 128, 128, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_state_aliasing_is_bitwise():
+    log("[S_T aliases S0]")
+    x = prefill_inputs(2, 200, 2, 128, 128, dtype="bf16", seed=27)
+    o1, s1 = run_prefill(x, "bf16", 64)
+    o2, s2 = run_prefill(x, "bf16", 64, alias=True)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_head_permutation():
+    log("[head permutation] bf16 H4")
+    x = prefill_inputs(1, 130, 4, 64, 64, dtype="bf16", seed=28)
+    perm = [3, 1, 0, 2]
+    xp = {n: (None if a is None else (a[:, perm] if n == "S0" else a[:, :, perm]))
+          for n, a in x.items()}
+    o, s = run_prefill(x, "bf16", 64)
+    op, sp = run_prefill(xp, "bf16", 64)
+    np.testing.assert_array_equal(op, o[:, :, perm])
+    np.testing.assert_array_equal(sp, s[:, perm])
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 16)])
+def test_p2_beta_zero_keeps_state_bitwise(dtype, C):
+    import torch
+    kda = _kda()
+    log(f"[P2 beta=0 alpha=1] {dtype} C{C}")
+    x = prefill_inputs(1, 3 * C + 7, 2, 128 if dtype == "bf16" else 64, 64, dtype=dtype, seed=29)
+    x["beta"][:] = 0.0
+    x["alpha"][:] = 1.0
+    o, st = run_prefill(x, dtype, C)
+    np.testing.assert_array_equal(st, x["S0"].astype(np.float64))
+    o_ref = np.einsum("bthi,bhij->bthj", x["q"].astype(np.float64), x["S0"].astype(np.float64))
+    assert rel_err(o, o_ref) <= TOL[dtype]
+    # the decode step as well
+    q, k, v, a, b = (to_dev(x[n][:, 0], dtype) for n in ("q", "k", "v", "alpha", "beta"))
+    S = torch.from_numpy(x["S0"]).cuda()
+    kda.kda_decode_step(q, k, v, a, b, S)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(S.cpu().numpy(), x["S0"])
+
+
+@pytest.mark.parametrize("dtype,d,kind", [("bf16", 16, "hadamard"), ("bf16", 64, "hadamard"),
+                                          ("f32", 64, "hadamard"), ("bf16", 128, "onehot")])
+def test_p1_orthonormal_recall(dtype, d, kind):
+    log(f"[P1 recall] {dtype} d{d} {kind}")
+    rng = np.random.default_rng(d)
+    T = 200
+    keys = orthonormal_key_set(d, kind)
+    kid, qid = rng.integers(0, d, T), rng.integers(0, d, T)
+    v = round_to_bf16(rng.standard_normal((T, d)).astype(np.float32))
+    last, expect = {}, np.zeros((T, d))
+    for t in range(T):
+        last[kid[t]] = v[t]
+        expect[t] = last.get(qid[t], np.zeros(d))
+    x = dict(q=keys[qid][None, :, None], k=keys[kid][None, :, None], v=v[None, :, None],
+             alpha=np.ones((1, T, 1, d), np.float32), beta=np.ones((1, T, 1), np.float32), S0=None)
+    o, st = run_prefill(x, dtype, 64 if d < 128 or dtype == "bf16" else 32)
+    e = rel_err(o[0, :, 0], expect)
+    log(f"[P1 recall] rel_err {e:.3e}")
+    assert e <= TOL[dtype]
+
+
+def test_golden_onehot_overwrite_on_gpu():
+    log("[golden one-hot overwrite] f32, d padded to 16")
+    g = overwrite_recall()
+    T, d = len(g["keys"]), 16
+    E = np.eye(d, dtype=np.float32)
+    v = np.zeros((T, d), np.float32); v[:, :4] = g["v"]
+    x = dict(q=E[g["queries"]][None, :, None], k=E[g["keys"]][None, :, None], v=v[None, :, None],
+             alpha=np.ones((1, T, 1, d), np.float32), beta=np.ones((1, T, 1), np.float32), S0=None)
+    o, st = run_prefill(x, "f32", 16)
+    np.testing.assert_allclose(o[0, :, 0, :4], g["o_expected"], atol=1e-6)
+    np.testing.assert_allclose(st[0, 0, :4, :4], g["S_expected"], atol=1e-6)
+
+
+def test_decode_alpha_zero_exact():
+    import torch
+    kda = _kda()
+    log("[decode alpha=0]")
+    x = prefill_inputs(3, 1, 2, 32, 16, dtype="f32", seed=30)
+    q, k, v, a, b = (to_dev(x[n][:, 0], "f32") for n in ("q", "k", "v", "alpha", "beta"))
+    a.zero_()
+    S = torch.from_numpy(x["S0"]).cuda()
+    o = kda.kda_decode_step(q, k, v, a, b, S)
+    torch.cuda.synchronize()
+    kk, qq, vv, bb = (x[n][:, 0].astype(np.float64) for n in ("k", "q", "v", "beta"))
+    S_ref = bb[..., None, None] * kk[..., :, None] * vv[..., None, :]
+    o_ref = (bb * np.sum(kk * qq, -1))[..., None] * vv
+    assert rel_err(S.cpu().numpy(), S_ref) <= 1e-6
+    assert rel_err(to_np(o), o_ref) <= 1e-6
