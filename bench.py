@@ -126,14 +126,17 @@ def bench_prefill(name: str, steps: int, warmup: int):
     del x
     o = torch.empty((w.B, w.T, w.H, w.d_v), dtype=d["q"].dtype, device="cuda")
     st = torch.empty((w.B, w.H, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    code = kda.KDA_BF16 if w.dtype == "bf16" else kda.KDA_F32
+    ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H, w.d_k, w.d_v, w.chunk, code),
+                     dtype=torch.uint8, device="cuda")
 
     def fn():
         kda.kda_fwd_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0, chunk=w.chunk,
-                            o=o, S_T=st)
+                            o=o, S_T=st, workspace=ws)
 
     total, per = _time_launches(fn, steps, warmup)
     ok = bool(torch.isfinite(o.float()).all().item() and torch.isfinite(st).all().item())
-    del d, o, st, s0
+    del d, o, st, s0, ws
     torch.cuda.empty_cache()
     return w, total, per, ok
 

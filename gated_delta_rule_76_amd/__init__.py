@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 __all__ = [
     "KDA_F32", "KDA_BF16", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
-    "status_string", "version",
+    "status_string", "version", "workspace_bytes",
 ]
 
 KDA_F32 = 0
@@ -125,13 +125,20 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def workspace_bytes(B: int, T: int, H: int, d_k: int, d_v: int, chunk: int, dtype: int) -> int:
+    return int(lib().kda_fwd_chunked_workspace_bytes(B, T, H, d_k, d_v, chunk, dtype))
+
+
 def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
-                    return_state: bool = True):
+                    return_state: bool = True, workspace=None):
     """Chunked KDA prefill on the GPU.
 
     q, k, alpha: [B,T,H,d_k]; v: [B,T,H,d_v]; beta: [B,T,H] (all bf16 or all
     fp32, CUDA/HIP tensors); S0: [B,H,d_k,d_v] fp32 or None.  Returns (o, S_T);
     S_T is None when return_state is False.  ``S_T`` may be S0 (in place).
+    ``workspace`` is an optional uint8 device tensor of at least
+    workspace_bytes(...) bytes; by default one is taken from torch's caching
+    allocator for the call.
     """
     torch = _torch()
     if q.dim() != 4:
@@ -155,11 +162,16 @@ def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S
         S_T = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
     if S_T is not None:
         _check(S_T, "S_T", (B, H, d_k, d_v), torch.float32, dev)
+    need = workspace_bytes(B, T, H, d_k, d_v, chunk, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError(f"workspace must hold {need} bytes on {dev}")
     st = kda_fwd_chunked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
                              beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
                              o.data_ptr(), S_T.data_ptr() if S_T is not None else None,
-                             B, T, H, d_k, d_v, chunk, _dtype_code(q), None, 0,
-                             _stream_handle(dev))
+                             B, T, H, d_k, d_v, chunk, _dtype_code(q), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream_handle(dev))
     if st != 0:
         raise KdaError(st, "kda_fwd_chunked")
     return o, S_T

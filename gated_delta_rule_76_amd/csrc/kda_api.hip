@@ -36,7 +36,14 @@ const char* kda_status_string(int status) {
   return "KDA_ERR_UNKNOWN";
 }
 
-size_t kda_fwd_chunked_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v, int chunk,
+                                       int dtype) {
+  if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+  size_t slot = 0;
+  if (!kda::prefill_slot_bytes(dtype == KDA_BF16, d_k, d_v, chunk, &slot)) return 0;
+  const size_t nchunk = (static_cast<size_t>(T) + chunk - 1) / chunk;
+  return static_cast<size_t>(B) * H * nchunk * slot;
+}
 
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
                     const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
@@ -56,12 +63,14 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alp
       if (reinterpret_cast<uintptr_t>(beta) % esz != 0) return KDA_ERR_INVALID_ARG;
     }
     if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return KDA_ERR_INVALID_ARG;
-    if (workspace_bytes < kda_fwd_chunked_workspace_bytes(B, T, H, d_k, d_v, chunk, dtype))
-      return KDA_ERR_WORKSPACE;
-    (void)workspace;
     // Token and state offsets are computed in 64-bit; keep grid sizes sane.
     if (static_cast<long long>(B) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (!kda::prefill_supported(dtype == KDA_BF16, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
+    const long long nchunk = (static_cast<long long>(T) + chunk - 1) / chunk;
+    if (static_cast<long long>(B) * H * nchunk > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+    const size_t need = kda_fwd_chunked_workspace_bytes(B, T, H, d_k, d_v, chunk, dtype);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+      return KDA_ERR_WORKSPACE;
     if (T == 0 && S_T == nullptr) return KDA_OK;
 
     kda::PrefillArgs a;
@@ -69,6 +78,7 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alp
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.chunk = chunk;
     a.bf16 = dtype == KDA_BF16;
+    a.workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
     return from_hip(kda::launch_prefill(a));
   } catch (...) {

@@ -21,6 +21,7 @@ struct PrefillArgs {
   float* S_T;
   int B, T, H, d_k, d_v, chunk;
   bool bf16;
+  void* workspace;  // kda_fwd_chunked_workspace_bytes() bytes of device memory
   hipStream_t stream;
 };
 
@@ -33,5 +34,10 @@ hipError_t launch_prefill(const PrefillArgs& a);
 
 // Whether a prefill kernel exists for this combination (host-only check).
 bool prefill_supported(bool bf16, int d_k, int d_v, int chunk);
+
+// Bytes of one chunk's workspace slot for this combination (false when the
+// combination is not compiled).  The prefill needs one slot per chunk of
+// every (batch, head): B * H * ceil(T / chunk) * slot bytes.
+bool prefill_slot_bytes(bool bf16, int d_k, int d_v, int chunk, size_t* slot);
 
 }  // namespace kda

@@ -81,8 +81,13 @@ KDA_API const char *kda_status_string(int status);
  *   d_k, d_v    : each one of 16, 32, 64, 128
  *   chunk       : one of 16, 32, 64 (KDA_F32 with d_k = 128 supports chunk
  *                 <= 32: its fp32 chunk tiles would not fit in LDS)
- *   workspace   : reserved; pass NULL and 0 (kda_fwd_chunked_workspace_bytes
- *                 returns the size a configuration needs, currently 0)
+ *   workspace   : device memory of at least kda_fwd_chunked_workspace_bytes()
+ *                 bytes, 16-byte aligned, owned by the caller.  It holds one
+ *                 slot of per-chunk operand tiles for every chunk of every
+ *                 (batch, head) between the two kernels of the call.  Its
+ *                 contents on entry are ignored and undefined on return;
+ *                 calls that share a workspace must not overlap in time.
+ *                 NULL or too small -> KDA_ERR_WORKSPACE.
  *
  * Semantics: T = 0 copies S0 (or zeros) to S_T and leaves o untouched.  A
  * last chunk shorter than `chunk` is handled exactly (padding tokens write
@@ -97,7 +102,10 @@ KDA_API int kda_fwd_chunked(const void *q, const void *k, const void *v, const v
                     int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace kda_fwd_chunked needs for these sizes (0 today). */
+/* Bytes of workspace kda_fwd_chunked needs for these sizes:
+ * B * H * ceil(T / chunk) * (bytes of one chunk's operand slot, about
+ * 65 KiB at d_k = d_v = 128, chunk = 64, bf16).  0 for an unsupported or
+ * invalid combination. */
 KDA_API size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                        int chunk, int dtype);
 

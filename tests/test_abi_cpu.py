@@ -31,8 +31,15 @@ def test_version_and_status_strings():
     assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
 
 
-def test_workspace_query_is_zero():
-    assert kda.lib().kda_fwd_chunked_workspace_bytes(4, 16384, 16, 128, 128, 64, kda.KDA_BF16) == 0
+def test_workspace_query():
+    ws = kda.lib().kda_fwd_chunked_workspace_bytes
+    one = ws(1, 64, 1, 128, 128, 64, kda.KDA_BF16)      # one chunk's slot
+    assert one % 1024 == 0 and 64 * 1024 <= one <= 66 * 1024
+    assert ws(4, 16384, 16, 128, 128, 64, kda.KDA_BF16) == 4 * 16 * 256 * one
+    assert ws(1, 65, 1, 128, 128, 64, kda.KDA_BF16) == 2 * one   # ragged tail: one more slot
+    assert ws(1, 0, 1, 128, 128, 64, kda.KDA_BF16) == 0
+    assert ws(1, 64, 1, 128, 128, 64, kda.KDA_F32) == 0          # unsupported combination
+    assert ws(1, 64, 1, 48, 128, 64, kda.KDA_BF16) == 0
 
 
 # Fake but 16-byte-aligned addresses: every call below must fail validation
@@ -42,11 +49,11 @@ P = 0x100000
 
 def _fwd(**kw):
     a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=None, o=P, S_T=P, B=1, T=64, H=1, d_k=64,
-             d_v=64, chunk=64, dtype=kda.KDA_BF16)
+             d_v=64, chunk=64, dtype=kda.KDA_BF16, ws=None, ws_bytes=0)
     a.update(kw)
     return kda.kda_fwd_chunked_raw(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], a["o"],
                                    a["S_T"], a["B"], a["T"], a["H"], a["d_k"], a["d_v"], a["chunk"],
-                                   a["dtype"])
+                                   a["dtype"], a["ws"], a["ws_bytes"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -60,6 +67,14 @@ def _fwd(**kw):
 ])
 def test_fwd_validation(kw, code):
     assert _fwd(**kw) == code
+
+
+def test_fwd_workspace_checks():
+    need = kda.lib().kda_fwd_chunked_workspace_bytes(1, 64, 1, 64, 64, 64, kda.KDA_BF16)
+    assert need > 0
+    assert _fwd() == 3                                   # no workspace
+    assert _fwd(ws=P, ws_bytes=need - 1) == 3            # too small
+    assert _fwd(ws=P + 8, ws_bytes=need) == 3            # misaligned
 
 
 def test_fwd_t0_without_state_is_a_no_op():
