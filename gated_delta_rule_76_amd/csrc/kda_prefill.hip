@@ -185,25 +185,33 @@ struct PrepCfg {
   static constexpr int NRG0 = NTH_PREP / NCG;
   static constexpr int NRG = NRG0 < C ? NRG0 : C;  // row groups in use
   static constexpr int RPG = C / NRG;               // rows per row group
-  static constexpr int LDK = DK + S::M::PAD;
-  static constexpr int LDC = C + S::M::PAD;
-  static constexpr int LDF = C + 4;  // fp32 C x C tiles (16-byte aligned rows)
+  static constexpr int LDK = DK + S::M::PAD;        // row stride of the C x DK tiles
+  static constexpr int LDF = C + 4;                 // fp32 C x C tiles (16-byte aligned rows)
+  static constexpr int NPAIR = S::NT * (S::NT + 1) / 2;  // lower-triangular 16x16 tiles
+  static constexpr int APW = (NPAIR + NW_PREP - 1) / NW_PREP;  // A tiles per wave
   static_assert(NRG * RPG == C && NCG * NRG <= NTH_PREP, "prologue map");
+  // LDS plan (bytes).  Four C x DK operand tiles live from tile formation to
+  // the end of the fragment stores.  The scan scratch is used before them,
+  // Mf and Xf after them, so both reuse the same bytes.
+  static constexpr int TILE = C * LDK * static_cast<int>(sizeof(lds_t));
+  static constexpr int MF = C * LDF * 4;
+  static constexpr int SCAN = NRG * DK * 4;
+  static constexpr int R_TILES = 4 * TILE;
+  static constexpr int R_AFTER = 2 * MF;
+  static constexpr int REGION = ((R_TILES > R_AFTER ? R_TILES : R_AFTER) > SCAN
+                                     ? (R_TILES > R_AFTER ? R_TILES : R_AFTER)
+                                     : SCAN);
+  static constexpr int OFF_KP = 0, OFF_KM = TILE, OFF_QP = 2 * TILE, OFF_KB = 3 * TILE;
+  static constexpr int OFF_MF = 0, OFF_XF = MF, OFF_SCAN = 0;
   struct Smem {
-    alignas(16) lds_t Kp[C * LDK];
-    alignas(16) lds_t Km[C * LDK];
-    alignas(16) lds_t Qp[C * LDK];
-    alignas(16) lds_t KbT[DK * LDC];
-    alignas(16) float Mf[C * LDF];  // Diag(beta) A, strictly lower
-    alignas(16) float Xf[C * LDF];  // (I + Diag(beta) A)^{-1}, lower
+    alignas(16) char region[REGION];
     alignas(16) float gC[DK];
     alignas(16) float beta[C];
-    alignas(16) float scan[NRG * DK];
   };
 };
 
 template <typename E, int DK, int C>
-__global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
+__global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ alpha, const typename E::storage* __restrict__ beta,
     char* __restrict__ ws, int T, int H, int nchunk, int ntask) {
@@ -214,15 +222,19 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
   using frag = typename S::frag;
   using St = typename E::storage;
   __shared__ typename P::Smem sm;
+  lds_t* const Kp = reinterpret_cast<lds_t*>(sm.region + P::OFF_KP);
+  lds_t* const Km = reinterpret_cast<lds_t*>(sm.region + P::OFF_KM);
+  lds_t* const Qp = reinterpret_cast<lds_t*>(sm.region + P::OFF_QP);
+  lds_t* const Kb = reinterpret_cast<lds_t*>(sm.region + P::OFF_KB);
+  float* const Mf = reinterpret_cast<float*>(sm.region + P::OFF_MF);
+  float* const Xf = reinterpret_cast<float*>(sm.region + P::OFF_XF);
+  float* const scan = reinterpret_cast<float*>(sm.region + P::OFF_SCAN);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const int cg = tid % P::NCG, rg = tid / P::NCG;
   const bool pro = rg < P::NRG;
   const int ch0 = 8 * cg;
-
-  // Upper parts of Mf and Xf are never written per chunk: zero them once.
-  for (int i = tid; i < C * P::LDF; i += NTH_PREP) { sm.Mf[i] = 0.f; sm.Xf[i] = 0.f; }
 
   // Token row of (task, r), clamped into the sequence so loads stay in bounds.
   auto rowptr = [&](int task, int r) -> long {
@@ -233,15 +245,19 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
   };
 
   Raw8<St> ra[P::RPG], rk[P::RPG], rq[P::RPG];
+  St rb = St(0);
   auto prefetch = [&](int task) {
-    if (task < ntask && pro) {
+    if (task < ntask) {
+      if (pro) {
 #pragma unroll
-      for (int rr = 0; rr < P::RPG; ++rr) {
-        const long row = rowptr(task, rg * P::RPG + rr);
-        ra[rr].load(alpha + row * DK + ch0);
-        rk[rr].load(k + row * DK + ch0);
-        rq[rr].load(q + row * DK + ch0);
+        for (int rr = 0; rr < P::RPG; ++rr) {
+          const long row = rowptr(task, rg * P::RPG + rr);
+          ra[rr].load(alpha + row * DK + ch0);
+          rk[rr].load(k + row * DK + ch0);
+          rq[rr].load(q + row * DK + ch0);
+        }
       }
+      if (tid < C) rb = beta[rowptr(task, tid)];
     }
   };
   prefetch(blockIdx.x);
@@ -252,8 +268,8 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
     char* slot = ws + static_cast<long>(task) * S::SLOT;
 
     // ---- 1. decay scan, from the prefetched registers
-    f32x8 lg[P::RPG], kk[P::RPG], qq[P::RPG];
-    __syncthreads();  // the previous task is done with every LDS tile
+    f32x8 lg[P::RPG];
+    __syncthreads();  // the previous task is done with every LDS byte
     if (pro) {
       f32x8 run;
 #pragma unroll
@@ -262,111 +278,104 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
       for (int rr = 0; rr < P::RPG; ++rr) {
         const bool ok = rg * P::RPG + rr < valid;
         const f32x8 a = ra[rr].unpack();
-        kk[rr] = rk[rr].unpack();
-        qq[rr] = rq[rr].unpack();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          run[e] *= ok ? a[e] : 1.f;
-          kk[rr][e] = ok ? kk[rr][e] : 0.f;
-          qq[rr][e] = ok ? qq[rr][e] : 0.f;
-        }
+        for (int e = 0; e < 8; ++e) run[e] *= ok ? a[e] : 1.f;
         lg[rr] = run;
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.scan[rg * DK + ch0 + e] = run[e];
+      for (int e = 0; e < 8; ++e) scan[rg * DK + ch0 + e] = run[e];
     }
-    if (tid < C) {
-      const float bv = load_scalar(beta, rowptr(task, tid));
-      sm.beta[tid] = tid < valid ? bv : 0.f;
-    }
-    prefetch(task + gridDim.x);  // next task's inputs load while this one computes
+    if (tid < C) sm.beta[tid] = tid < valid ? load_scalar(&rb, 0) : 0.f;
     __syncthreads();
     if (tid < DK) {  // exclusive products of the row-group totals, per channel
       float tot[P::NRG];
 #pragma unroll
-      for (int gg = 0; gg < P::NRG; ++gg) tot[gg] = sm.scan[gg * DK + tid];
+      for (int gg = 0; gg < P::NRG; ++gg) tot[gg] = scan[gg * DK + tid];
       float p = 1.f;
 #pragma unroll
       for (int gg = 0; gg < P::NRG; ++gg) {
-        sm.scan[gg * DK + tid] = p;
+        scan[gg * DK + tid] = p;
         p *= tot[gg];
       }
       sm.gC[tid] = p;
     }
     __syncthreads();
-
-    // ---- 2. decay-scaled operand tiles
+    f32x8 pre, gc;
     if (pro) {
-      f32x8 pre, gc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { pre[e] = sm.scan[rg * DK + ch0 + e]; gc[e] = sm.gC[ch0 + e]; }
+      for (int e = 0; e < 8; ++e) { pre[e] = scan[rg * DK + ch0 + e]; gc[e] = sm.gC[ch0 + e]; }
+    }
+    __syncthreads();  // the scan scratch is about to be overwritten by the tiles
+
+    // ---- 2. decay-scaled operand tiles, all row-major [r][channel]
+    if (pro) {
 #pragma unroll
       for (int rr = 0; rr < P::RPG; ++rr) {
         const int r = rg * P::RPG + rr;
-        f32x8 kp, qp, km;
+        const bool ok = r < valid;  // rows past the sequence: k = q = 0
+        const f32x8 kk = rk[rr].unpack(), qq = rq[rr].unpack();
+        f32x8 kp, qp, km, kb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float gam = lg[rr][e] * pre[e];
           const float inv = __builtin_amdgcn_rcpf(gam);
-          kp[e] = kk[rr][e] * gam;
-          qp[e] = qq[rr][e] * gam;
-          km[e] = kk[rr][e] * inv;
+          const float kv = ok ? kk[e] : 0.f, qv = ok ? qq[e] : 0.f;
+          kp[e] = kv * gam;
+          qp[e] = qv * gam;
+          km[e] = kv * inv;
+          kb[e] = km[e] * gc[e];
         }
-        M::store8(&sm.Kp[r * P::LDK + ch0], kp);
-        M::store8(&sm.Qp[r * P::LDK + ch0], qp);
-        M::store8(&sm.Km[r * P::LDK + ch0], km);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.KbT[(ch0 + e) * P::LDC + r] = M::cvt(km[e] * gc[e]);
+        M::store8(&Kp[r * P::LDK + ch0], kp);
+        M::store8(&Qp[r * P::LDK + ch0], qp);
+        M::store8(&Km[r * P::LDK + ch0], km);
+        M::store8(&Kb[r * P::LDK + ch0], kb);
       }
     }
+    prefetch(task + gridDim.x);  // next task's inputs load while this one computes
     __syncthreads();
 
-    // ---- 3. Gram tiles, P fragments, and the K+ / Q+ / Kbar^T fragments
+    // ---- 3. Gram tiles (kept in registers), P fragments, and the K+ / Q+ /
+    //         Kbar^T fragments copied into the workspace slot
+    f32x4 Aacc[P::APW];
     {
-      // A tile (tr, tc), tc <= tr: A[16tr+4g+e][16tc+c16] -> Diag(beta) A, fp32 LDS.
-      constexpr int NPAIR = S::NT * (S::NT + 1) / 2;
       int job = 0;
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
         for (int tc = 0; tc <= tr; ++tc, ++job) {
           if (job % NW_PREP != wave) continue;
-          const lds_t* arow = sm.Kp + (16 * tr + c16) * P::LDK;
-          const lds_t* brow = sm.Km + (16 * tc + c16) * P::LDK;
+          const lds_t* arow = Kp + (16 * tr + c16) * P::LDK;
+          const lds_t* brow = Km + (16 * tc + c16) * P::LDK;
           frag af[S::NKS], bf[S::NKS];
 #pragma unroll
-          for (int s = 0; s < S::NKS; ++s) {
-            const int kb = 32 * s + 4 * g;
-            const bool h = S::KODD && s == S::NKS - 1;
-            af[s] = h ? M::half(arow + kb) : M::pair(arow + kb, arow + kb + 16);
-            bf[s] = h ? M::half(brow + kb) : M::pair(brow + kb, brow + kb + 16);
+          for (int s2 = 0; s2 < S::NKS; ++s2) {
+            const int kb = 32 * s2 + 4 * g;
+            const bool h = S::KODD && s2 == S::NKS - 1;
+            af[s2] = h ? M::half(arow + kb) : M::pair(arow + kb, arow + kb + 16);
+            bf[s2] = h ? M::half(brow + kb) : M::pair(brow + kb, brow + kb + 16);
           }
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < S::NKS; ++s) acc = M::mma(af[s], bf[s], acc);
-          const int jc = 16 * tc + c16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tr + 4 * g + e;
-            sm.Mf[r * P::LDF + jc] = jc < r ? sm.beta[r] * acc[e] : 0.f;
-          }
+          for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(af[s2], bf[s2], acc);
+          Aacc[job / NW_PREP] = acc;  // job % NW_PREP == wave
         }
+      job = 0;
       // P fragments (tr, s), s <= tr/2, from P^T tiles: the accumulator of
       // the product K- Q+^T holds P[16tr+c16][16tc+4g+e] in lane (g, c16),
       // i.e. exactly the operand order.
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int s = 0; s <= tr / 2; ++s, ++job) {
-          if (job % NW_PREP != wave) continue;
-          const lds_t* brow = sm.Qp + (16 * tr + c16) * P::LDK;
+        for (int s2 = 0; s2 <= tr / 2; ++s2, ++job) {
+          if ((job + 1) % NW_PREP != wave) continue;
+          const lds_t* brow = Qp + (16 * tr + c16) * P::LDK;
           f32x4 half_acc[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int tc = 2 * s + hh;
+            const int tc = 2 * s2 + hh;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (tc <= tr) {
-              const lds_t* arow = sm.Km + (16 * tc + c16) * P::LDK;
+              const lds_t* arow = Km + (16 * tc + c16) * P::LDK;
               frag af[S::NKS], bf[S::NKS];
 #pragma unroll
               for (int ks = 0; ks < S::NKS; ++ks) {
@@ -383,47 +392,67 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
             }
             half_acc[hh] = acc;
           }
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (tr * S::NCS + s) * S::FRAG);
+          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (tr * S::NCS + s2) * S::FRAG);
           dst[lane] = M::from_acc(half_acc[0], half_acc[1]);
         }
-      // K+, Q+ fragments (rows r, k = channels) and Kbar^T fragments (rows =
-      // channels, k = r) copied from LDS into the workspace.
+      // K+ and Q+ fragments: rows r, k = channels.
+      constexpr int NKQ = 2 * S::NT * S::NKS;
+      for (int jj = wave; jj < NKQ; jj += NW_PREP) {
+        const int w2 = jj & 1, ts = jj >> 1;  // ts = t * NKS + s
+        const int t = ts / S::NKS, s2 = ts - t * S::NKS;
+        const lds_t* row = (w2 ? Qp : Kp) + (16 * t + c16) * P::LDK;
+        const int kb = 32 * s2 + 4 * g;
+        const frag f = (S::KODD && s2 == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
+        reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane] = f;
+      }
+      // Kbar^T fragments: rows = channels 16t + c16, k = token rows, gathered
+      // down a column of the row-major Kbar tile.
+      constexpr int NKB = S::NTK * S::NCS;
+      for (int jj = wave; jj < NKB; jj += NW_PREP) {
+        const int t = jj / S::NCS, s2 = jj - t * S::NCS;
+        const lds_t* colp = Kb + 16 * t + c16;
+        const int r0 = 32 * s2 + 4 * g;
+        frag f;
 #pragma unroll
-      for (int t = 0; t < S::NT; ++t)
+        for (int e = 0; e < 4; ++e) f[e] = colp[(r0 + e) * P::LDK];
+        if (S::CODD && s2 == S::NCS - 1) {
 #pragma unroll
-        for (int s = 0; s < S::NKS; ++s)
+          for (int e = 0; e < 4; ++e) f[4 + e] = M::cvt(0.f);
+        } else {
 #pragma unroll
-          for (int w2 = 0; w2 < 2; ++w2, ++job) {
-            if (job % NW_PREP != wave) continue;
-            const lds_t* row = (w2 ? sm.Qp : sm.Kp) + (16 * t + c16) * P::LDK;
-            const int kb = 32 * s + 4 * g;
-            const frag f = (S::KODD && s == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
-            frag* dst = reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + (t * S::NKS + s) * S::FRAG);
-            dst[lane] = f;
-          }
-#pragma unroll
-      for (int t = 0; t < S::NTK; ++t)
-#pragma unroll
-        for (int s = 0; s < S::NCS; ++s, ++job) {
-          if (job % NW_PREP != wave) continue;
-          const lds_t* row = sm.KbT + (16 * t + c16) * P::LDC;
-          const int kb = 32 * s + 4 * g;
-          const frag f = (S::CODD && s == S::NCS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_KB + (t * S::NCS + s) * S::FRAG);
-          dst[lane] = f;
+          for (int e = 0; e < 4; ++e) f[4 + e] = colp[(r0 + 16 + e) * P::LDK];
         }
-      (void)NPAIR;
+        reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane] = f;
+      }
       if (tid < DK) reinterpret_cast<float*>(slot + S::OFF_GC)[tid] = sm.gC[tid];
     }
-    __syncthreads();
+    __syncthreads();  // the operand tiles are dead: Mf and Xf take their bytes
 
-    // ---- 4. X = (I + Mf)^{-1}: diagonal 16x16 blocks by substitution
+    // ---- 4. Mf = Diag(beta) strict_lower(A), then X = (I + Mf)^{-1}
+    {
+      int job = 0;
+#pragma unroll
+      for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+        for (int tc = 0; tc <= tr; ++tc, ++job) {
+          if (job % NW_PREP != wave) continue;
+          const f32x4 acc = Aacc[job / NW_PREP];
+          const int jc = 16 * tc + c16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tr + 4 * g + e;
+            Mf[r * P::LDF + jc] = jc < r ? sm.beta[r] * acc[e] : 0.f;
+          }
+        }
+    }
+    __syncthreads();
+    // diagonal 16x16 blocks by substitution, one wave per block
     for (int bi = wave; bi < S::NT; bi += NW_PREP) {
       if (lane < 16) {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float* mrow = &sm.Mf[(16 * bi + r) * P::LDF + 16 * bi];
+          const float* mrow = &Mf[(16 * bi + r) * P::LDF + 16 * bi];
           float m[16];
 #pragma unroll
           for (int j = 0; j < r; ++j) m[j] = mrow[j];
@@ -436,7 +465,7 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
           x[r] = a0 + a1;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Xf[(16 * bi + r) * P::LDF + 16 * bi + lane] = x[r];
+        for (int r = 0; r < 16; ++r) Xf[(16 * bi + r) * P::LDF + 16 * bi + lane] = x[r];
       }
     }
     // off-diagonal blocks, one distance at a time:
@@ -450,48 +479,50 @@ __global__ __launch_bounds__(NTH_PREP) void chunk_prep_kernel(
         for (int cc = bb; cc < aa; ++cc) {
           float av[4], bv[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            av[s] = sm.Mf[(16 * aa + c16) * P::LDF + 16 * cc + 4 * s + g];
-            bv[s] = sm.Xf[(16 * cc + 4 * s + g) * P::LDF + 16 * bb + c16];
+          for (int s2 = 0; s2 < 4; ++s2) {
+            av[s2] = Mf[(16 * aa + c16) * P::LDF + 16 * cc + 4 * s2 + g];
+            bv[s2] = Xf[(16 * cc + 4 * s2 + g) * P::LDF + 16 * bb + c16];
           }
 #pragma unroll
-          for (int s = 0; s < 4; ++s) y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], y, 0, 0, 0);
+          for (int s2 = 0; s2 < 4; ++s2) y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], bv[s2], y, 0, 0, 0);
         }
         float av[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) av[s] = sm.Xf[(16 * aa + c16) * P::LDF + 16 * aa + 4 * g + s];
+        for (int s2 = 0; s2 < 4; ++s2) av[s2] = Xf[(16 * aa + c16) * P::LDF + 16 * aa + 4 * g + s2];
         f32x4 xo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], y[s], xo, 0, 0, 0);
+        for (int s2 = 0; s2 < 4; ++s2) xo = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s2], y[s2], xo, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Xf[(16 * aa + 4 * g + e) * P::LDF + 16 * bb + c16] = -xo[e];
+        for (int e = 0; e < 4; ++e) Xf[(16 * aa + 4 * g + e) * P::LDF + 16 * bb + c16] = -xo[e];
       }
     }
     __syncthreads();
 
-    // ---- 5. Tm = X Diag(beta) fragments (rows r, k = columns), s <= tr/2
+    // ---- 5. Tm = X Diag(beta) fragments (rows r, k = columns), s <= tr/2.
+    //         X is lower triangular: entries above the diagonal are masked.
     {
       int job = 0;
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int s = 0; s <= tr / 2; ++s, ++job) {
+        for (int s2 = 0; s2 <= tr / 2; ++s2, ++job) {
           if (job % NW_PREP != wave) continue;
-          const float* xrow = sm.Xf + (16 * tr + c16) * P::LDF;
-          const int kb = 32 * s + 4 * g;
+          const int r = 16 * tr + c16;
+          const float* xrow = Xf + r * P::LDF;
+          const int kb = 32 * s2 + 4 * g;
           f32x8 t8;
           const f32x4 lo = *reinterpret_cast<const f32x4*>(xrow + kb);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t8[e] = lo[e] * sm.beta[kb + e];
-          if (S::CODD && s == S::NCS - 1) {
+          for (int e = 0; e < 4; ++e) t8[e] = kb + e <= r ? lo[e] * sm.beta[kb + e] : 0.f;
+          if (S::CODD && s2 == S::NCS - 1) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) t8[4 + e] = 0.f;
           } else {
             const f32x4 hi = *reinterpret_cast<const f32x4*>(xrow + kb + 16);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t8[4 + e] = hi[e] * sm.beta[kb + 16 + e];
+            for (int e = 0; e < 4; ++e) t8[4 + e] = kb + 16 + e <= r ? hi[e] * sm.beta[kb + 16 + e] : 0.f;
           }
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (tr * S::NCS + s) * S::FRAG);
+          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (tr * S::NCS + s2) * S::FRAG);
           dst[lane] = M::from8(t8);
         }
     }
@@ -504,12 +535,25 @@ constexpr size_t kLdsLimit = 160 * 1024;
 template <typename E, int DK, int DVB, int C>
 struct PassCfg {
   using S = Shape<E, DK, C>;
-  static constexpr int NWB = DVB / 16;  // one wave per 16-column slab
-  static constexpr int NTH = 64 * NWB;
+  static constexpr int NC = DVB / 16;  // compute waves: one per 16-column slab
+  static constexpr int NTH = 64 * (NC + 1);  // plus one copy wave
   static constexpr int SLOT = S::SLOT;
-  // Double-buffer the slot when two fit in LDS, else stream it after compute.
-  static constexpr int NBUF = 2 * static_cast<size_t>(SLOT) <= kLdsLimit ? 2 : 1;
-  static constexpr size_t smem_bytes = NBUF * static_cast<size_t>(SLOT);
+  static constexpr int ESZ = static_cast<int>(sizeof(typename E::storage));
+  // Value / output tiles of one chunk: C rows x DVB columns, row-major,
+  // copied one 1 KiB wave instruction at a time (the last may run past row
+  // C into the tile's padding).
+  static constexpr int VROW = DVB * ESZ;                 // bytes per tile row
+  static constexpr int LPR = VROW / 16;                  // 16-byte lanes per row
+  static constexpr int RPI = 64 / LPR;                   // rows per wave instruction
+  static constexpr int NVI = (C + RPI - 1) / RPI;        // instructions per tile
+  static constexpr int VTILE = NVI * 1024;               // bytes per tile buffer
+  static_assert(VROW % 16 == 0 && 64 % LPR == 0, "tile copy map");
+  // Double-buffer the slot when two fit next to the value / output tiles.
+  static constexpr int NBUF =
+      2 * static_cast<size_t>(SLOT) + 4 * static_cast<size_t>(VTILE) <= kLdsLimit ? 2 : 1;
+  static constexpr int OFF_V = NBUF * SLOT;
+  static constexpr int OFF_O = OFF_V + 2 * VTILE;
+  static constexpr size_t smem_bytes = static_cast<size_t>(OFF_O) + 2 * VTILE;
 };
 
 template <typename E, int DK, int DVB, int C>
@@ -521,144 +565,185 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
   using K = PassCfg<E, DK, DVB, C>;
   using M = typename S::M;
   using frag = typename S::frag;
+  using St = typename E::storage;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int chain = blockIdx.x, vb = blockIdx.y;
   const int b = chain / H, h = chain - b * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, g = lane >> 4;
-  const int col = vb * DVB + 16 * wave + c16;
-  const long bh = chain;
-  auto tok = [&](int t) -> long { return (static_cast<long>(b) * T + t) * H + h; };
-  const char* wsb = ws + static_cast<long>(chain) * nchunk * K::SLOT;
+  const bool copier = wave == K::NC;
+  const long rs = static_cast<long>(H) * DV;  // element stride between tokens
+  const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
 
-  // Copy one workspace slot into LDS half `buf`, 1 KiB per wave instruction.
-  auto stage = [&](int n, int buf) {
-    const char* src = wsb + static_cast<long>(n) * K::SLOT;
+  // ------------------------------------------------------------ copy wave
+  // Lane map of a value/output tile row: lane l covers row (l / LPR) of the
+  // instruction's RPI rows, bytes 16 * (l % LPR) of it.
+  const int crow = lane / K::LPR, cbyte = 16 * (lane % K::LPR);
+  auto stage_slot = [&](int n, int buf) {
+    const char* src = ws + (static_cast<long>(chain) * nchunk + n) * K::SLOT;
     char* dst = lds + buf * K::SLOT;
-    for (int u = wave; u < K::SLOT / 1024; u += K::NWB)
+    for (int u = 0; u < K::SLOT / 1024; ++u)
       __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)(dst + u * 1024), 16, 0, 0);
   };
-  auto load_v = [&](int n, f32x4* R) {
+  auto stage_v = [&](int n) {
+    char* dst = lds + K::OFF_V + (n & 1) * K::VTILE;
 #pragma unroll
-    for (int tr = 0; tr < S::NT; ++tr)
+    for (int u = 0; u < K::NVI; ++u) {
+      const int t = min(n * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
+      const char* src = reinterpret_cast<const char*>(v + base + t * rs) + cbyte;
+      __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
+    }
+  };
+  auto store_out = [&](int n) {
+    const char* src = lds + K::OFF_O + (n & 1) * K::VTILE;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = n * C + 16 * tr + 4 * g + e;
-        const float x = load_scalar(v, tok(min(t, T - 1)) * DV + col);
-        R[tr][e] = t < T ? x : 0.f;
-      }
+    for (int u = 0; u < K::NVI; ++u) {
+      const int r = u * K::RPI + crow, t = n * C + r;
+      const uint4 x = *reinterpret_cast<const uint4*>(src + u * 1024 + lane * 16);
+      if (r < C && t < T) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x;
+    }
   };
 
-  // State slab as accumulator tiles: Sa[ti] holds S[16 ti + 4 g + e][col].
-  f32x4 Sa[S::NTK];
+  // --------------------------------------------------------- compute waves
+  const int c16 = lane & 15, g = lane >> 4;
+  const int lcol = 16 * wave + c16;  // column inside the value block
+  const int col = vb * DVB + lcol;
+  f32x4 Sa[S::NTK];  // Sa[ti] holds S[16 ti + 4 g + e][col]
+  if (!copier) {
+    if (S0 != nullptr) {
+      const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
-  for (int ti = 0; ti < S::NTK; ++ti)
+      for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Sa[ti][e] = S0 != nullptr ? S0[(bh * DK + 16 * ti + 4 * g + e) * DV + col] : 0.f;
-
-  f32x4 Rn[S::NT];
-  if (nchunk > 0) {
-    stage(0, 0);
-    load_v(0, Rn);
+        for (int e = 0; e < 4; ++e) Sa[ti][e] = s0[(16 * ti + e) * DV];
+    } else {
+#pragma unroll
+      for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  } else if (nchunk > 0) {
+    stage_slot(0, 0);
+    stage_v(0);
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  for (int n = 0; n < nchunk; ++n) {
-    f32x4 R[S::NT];
-#pragma unroll
-    for (int tr = 0; tr < S::NT; ++tr) R[tr] = Rn[tr];
-    __builtin_amdgcn_s_waitcnt(0);  // this chunk's slot has landed in LDS
-    __syncthreads();                // ... for every wave; the other half is free
-    if (n + 1 < nchunk) {
-      if (K::NBUF == 2) stage(n + 1, (n + 1) & 1);
-      load_v(n + 1, Rn);
-    }
-    const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
-    auto fr = [&](int off, int idx) -> frag {
-      return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
-    };
-    const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
-    const int t0 = n * C;
 
-    frag sfr[S::NKS];
+  for (int n = 0; n < nchunk; ++n) {
+    __syncthreads();  // slot n and values n are in LDS; output n-1 is in LDS
+    if (copier) {
+      if (n > 0) store_out(n - 1);
+      if (n + 1 < nchunk) {
+        if (K::NBUF == 2) stage_slot(n + 1, (n + 1) & 1);
+        stage_v(n + 1);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      const int t0 = n * C;
+      const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
+      auto fr = [&](int off, int idx) -> frag {
+        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
+      };
+      const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
+      const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
+      St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
+
+      f32x4 R[S::NT];
 #pragma unroll
-    for (int s = 0; s < S::NKS; ++s) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      sfr[s] = M::from_acc(Sa[2 * s], (S::KODD && s == S::NKS - 1) ? z : Sa[2 * s + 1]);
-    }
-    // R = V - K+ S
+      for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-    for (int tr = 0; tr < S::NT; ++tr) {
-      frag a[S::NKS];
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tr + 4 * g + e;
+          const float x = load_scalar(vt, r * DVB + lcol);
+          R[tr][e] = t0 + r < T ? x : 0.f;
+        }
+      frag sfr[S::NKS];
 #pragma unroll
-      for (int s = 0; s < S::NKS; ++s) a[s] = fr(S::OFF_KP, tr * S::NKS + s);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < S::NKS; ++s2) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        sfr[s2] = M::from_acc(Sa[2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[2 * s2 + 1]);
+      }
+      // R = V - K+ S
 #pragma unroll
-      for (int s = 0; s < S::NKS; ++s) acc = M::mma(a[s], sfr[s], acc);
-      R[tr] -= acc;
-    }
-    frag rfr[S::NCS];
+      for (int tr = 0; tr < S::NT; ++tr) {
+        frag a[S::NKS];
 #pragma unroll
-    for (int s = 0; s < S::NCS; ++s) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      rfr[s] = M::from_acc(R[2 * s], (S::CODD && s == S::NCS - 1) ? z : R[2 * s + 1]);
-    }
-    // U = Tm R  (Tm lower triangular: k-steps up to the diagonal tile)
-    f32x4 U[S::NT];
+        for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_KP, tr * S::NKS + s2);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tr = 0; tr < S::NT; ++tr) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[s2], acc);
+        R[tr] -= acc;
+      }
+      frag rfr[S::NCS];
 #pragma unroll
-      for (int s = 0; s <= tr / 2; ++s) acc = M::mma(fr(S::OFF_TM, tr * S::NCS + s), rfr[s], acc);
-      U[tr] = acc;
-    }
-    frag ufr[S::NCS];
+      for (int s2 = 0; s2 < S::NCS; ++s2) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        rfr[s2] = M::from_acc(R[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[2 * s2 + 1]);
+      }
+      // U = Tm R  (Tm lower triangular: k-steps up to the diagonal tile)
+      f32x4 U[S::NT];
 #pragma unroll
-    for (int s = 0; s < S::NCS; ++s) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      ufr[s] = M::from_acc(U[2 * s], (S::CODD && s == S::NCS - 1) ? z : U[2 * s + 1]);
-    }
-    // O = Q+ S + P U
+      for (int tr = 0; tr < S::NT; ++tr) {
+        frag a[S::NCS];
 #pragma unroll
-    for (int tr = 0; tr < S::NT; ++tr) {
-      frag a[S::NKS];
+        for (int s2 = 0; s2 <= tr / 2; ++s2) a[s2] = fr(S::OFF_TM, tr * S::NCS + s2);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < S::NKS; ++s) a[s] = fr(S::OFF_QP, tr * S::NKS + s);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(a[s2], rfr[s2], acc);
+        U[tr] = acc;
+      }
+      frag ufr[S::NCS];
 #pragma unroll
-      for (int s = 0; s < S::NKS; ++s) acc = M::mma(a[s], sfr[s], acc);
+      for (int s2 = 0; s2 < S::NCS; ++s2) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        ufr[s2] = M::from_acc(U[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[2 * s2 + 1]);
+      }
+      // O = Q+ S + P U, into the output tile
 #pragma unroll
-      for (int s = 0; s <= tr / 2; ++s) acc = M::mma(fr(S::OFF_PP, tr * S::NCS + s), ufr[s], acc);
+      for (int tr = 0; tr < S::NT; ++tr) {
+        frag a[S::NKS], p[S::NCS];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 16 * tr + 4 * g + e;
-        if (t < T) store_scalar(o, tok(t) * DV + col, acc[e]);
+        for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_QP, tr * S::NKS + s2);
+#pragma unroll
+        for (int s2 = 0; s2 <= tr / 2; ++s2) p[s2] = fr(S::OFF_PP, tr * S::NCS + s2);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[s2], acc);
+#pragma unroll
+        for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(p[s2], ufr[s2], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_scalar(ot, (16 * tr + 4 * g + e) * DVB + lcol, acc[e]);
+      }
+      // S <- Diag(gamma_C) S + Kbar^T U
+#pragma unroll
+      for (int ti = 0; ti < S::NTK; ++ti) {
+        frag a[S::NCS];
+#pragma unroll
+        for (int s2 = 0; s2 < S::NCS; ++s2) a[s2] = fr(S::OFF_KB, ti * S::NCS + s2);
+        f32x4 acc = Sa[ti];
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
+        acc *= gc;
+#pragma unroll
+        for (int s2 = 0; s2 < S::NCS; ++s2) acc = M::mma(a[s2], ufr[s2], acc);
+        Sa[ti] = acc;
       }
     }
-    // S <- Diag(gamma_C) S + Kbar^T U
-#pragma unroll
-    for (int ti = 0; ti < S::NTK; ++ti) {
-      frag a[S::NCS];
-#pragma unroll
-      for (int s = 0; s < S::NCS; ++s) a[s] = fr(S::OFF_KB, ti * S::NCS + s);
-      f32x4 acc = Sa[ti];
-      const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
-      acc *= gc;
-#pragma unroll
-      for (int s = 0; s < S::NCS; ++s) acc = M::mma(a[s], ufr[s], acc);
-      Sa[ti] = acc;
-    }
     if (K::NBUF == 1 && n + 1 < nchunk) {
-      __syncthreads();  // every wave is done with the single slot
-      stage(n + 1, 0);
+      __syncthreads();  // every compute wave is done with the single slot
+      if (copier) {
+        stage_slot(n + 1, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+      }
     }
   }
+  if (nchunk > 0) {
+    __syncthreads();  // the last output tile is in LDS
+    if (copier) store_out(nchunk - 1);
+  }
 
-  if (ST != nullptr) {
+  if (!copier && ST != nullptr) {
+    float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
     for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ST[(bh * DK + 16 * ti + 4 * g + e) * DV + col] = Sa[ti][e];
+      for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
   }
 }
 
@@ -670,8 +755,9 @@ constexpr int dvb_for(int dv) { return dv < 32 ? dv : 32; }
 
 template <typename E, int DK, int C>
 constexpr bool fits() {
-  return sizeof(typename PrepCfg<E, DK, C>::Smem) <= kLdsLimit &&
-         static_cast<size_t>(Shape<E, DK, C>::SLOT) <= kLdsLimit;
+  return sizeof(typename PrepCfg<E, DK, C>::Smem) <= kLdsLimit / 2 &&
+         PassCfg<E, DK, 32, C>::smem_bytes <= kLdsLimit &&
+         PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit;
 }
 
 template <typename E, int DK, int C>
@@ -698,7 +784,8 @@ hipError_t launch_t(const PrefillArgs& a) {
   const long ntask = static_cast<long>(a.B) * a.H * nchunk;
   char* ws = static_cast<char*>(a.workspace);
   if (ntask > 0) {
-    const int grid = static_cast<int>(ntask < num_cus() ? ntask : num_cus());
+    // two resident workgroups per CU, each walking a strided list of chunks
+    const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
     hipLaunchKernelGGL((chunk_prep_kernel<E, DK, C>), dim3(grid), dim3(NTH_PREP), 0, a.stream,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                        static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
