@@ -161,6 +161,12 @@ struct Shape {
   static constexpr bool KODD = (NTK & 1) != 0;
   static constexpr int NCS = (NT + 1) / 2;   // 32-wide k-steps over the chunk
   static constexpr bool CODD = (NT & 1) != 0;
+  // Lower-triangular C x C operands keep only the fragments (tr, s) with
+  // s <= tr / 2; tri(tr) = sum_{t < tr} (t / 2 + 1) is the index of (tr, 0)
+  // in that list.
+  static constexpr __host__ __device__ int tri(int tr) { return tr + ((tr - 1) * (tr - 1)) / 4; }
+  static_assert(tri(0) == 0 && tri(1) == 1 && tri(2) == 2 && tri(3) == 4 && tri(4) == 6, "tri");
+  static constexpr int NTRI = tri(NT);
   // Workspace slot: operand tiles as [tile][k-step][lane] fragments.
   static constexpr int FB = 8 * static_cast<int>(sizeof(lds_t));  // bytes per lane fragment
   static constexpr int FRAG = 64 * FB;                              // bytes per wave fragment
@@ -168,8 +174,8 @@ struct Shape {
   static constexpr int OFF_QP = OFF_KP + NT * NKS * FRAG;
   static constexpr int OFF_KB = OFF_QP + NT * NKS * FRAG;
   static constexpr int OFF_TM = OFF_KB + NTK * NCS * FRAG;
-  static constexpr int OFF_PP = OFF_TM + NT * NCS * FRAG;
-  static constexpr int OFF_GC = OFF_PP + NT * NCS * FRAG;
+  static constexpr int OFF_PP = OFF_TM + NTRI * FRAG;
+  static constexpr int OFF_GC = OFF_PP + NTRI * FRAG;
   static constexpr int SLOT = ((OFF_GC + DK * 4) + 1023) / 1024 * 1024;  // whole 1 KiB copy units
 };
 
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
             }
             half_acc[hh] = acc;
           }
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (tr * S::NCS + s2) * S::FRAG);
+          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (S::tri(tr) + s2) * S::FRAG);
           dst[lane] = M::from_acc(half_acc[0], half_acc[1]);
         }
       // K+ and Q+ fragments: rows r, k = channels.
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) t8[4 + e] = kb + 16 + e <= r ? hi[e] * sm.beta[kb + 16 + e] : 0.f;
           }
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (tr * S::NCS + s2) * S::FRAG);
+          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (S::tri(tr) + s2) * S::FRAG);
           dst[lane] = M::from8(t8);
         }
     }
@@ -535,8 +541,11 @@ constexpr size_t kLdsLimit = 160 * 1024;
 template <typename E, int DK, int DVB, int C>
 struct PassCfg {
   using S = Shape<E, DK, C>;
-  static constexpr int NC = DVB / 16;  // compute waves: one per 16-column slab
-  static constexpr int NTH = 64 * (NC + 1);  // plus one copy wave
+  static constexpr int NSLAB = DVB / 16;                 // 16-column state slabs
+  static constexpr int NCW = NSLAB < 4 ? NSLAB : 4;      // compute waves
+  static constexpr int SPW = NSLAB / NCW;                // slabs per compute wave
+  static constexpr int NCP = 6;                          // copy waves (loads)
+  static constexpr int NTH = 64 * (NCW + NCP + 1);       // + one store wave
   static constexpr int SLOT = S::SLOT;
   static constexpr int ESZ = static_cast<int>(sizeof(typename E::storage));
   // Value / output tiles of one chunk: C rows x DVB columns, row-major,
@@ -547,8 +556,9 @@ struct PassCfg {
   static constexpr int RPI = 64 / LPR;                   // rows per wave instruction
   static constexpr int NVI = (C + RPI - 1) / RPI;        // instructions per tile
   static constexpr int VTILE = NVI * 1024;               // bytes per tile buffer
-  static_assert(VROW % 16 == 0 && 64 % LPR == 0, "tile copy map");
-  // Double-buffer the slot when two fit next to the value / output tiles.
+  static_assert(VROW % 16 == 0 && 64 % LPR == 0 && NSLAB % NCW == 0, "pass map");
+  // Double-buffer the slot when two fit next to the (double-buffered)
+  // value and output tiles.
   static constexpr int NBUF =
       2 * static_cast<size_t>(SLOT) + 4 * static_cast<size_t>(VTILE) <= kLdsLimit ? 2 : 1;
   static constexpr int OFF_V = NBUF * SLOT;
@@ -556,6 +566,16 @@ struct PassCfg {
   static constexpr size_t smem_bytes = static_cast<size_t>(OFF_O) + 2 * VTILE;
 };
 
+// One workgroup per (batch, head, block of DVB value columns).  Compute
+// waves own SPW 16-column slabs of the fp32 state each; copy waves move the
+// workspace slot and the value tile into LDS; a store wave writes the output
+// tile out of it.  Value and output tiles are double-buffered, the slot too
+// when it fits, so one barrier per chunk suffices:
+//   [A] slot n and values n are in LDS, output n-1 is complete in LDS
+//   copy: start slot n+1 and values n+1, wait for them
+//   store: read output n-1 from LDS, issue its global stores (never waited
+//          on inside the loop; drained once before the wave ends)
+//   compute: values n into registers, the five products, output n into LDS
 template <typename E, int DK, int DVB, int C>
 __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kernel(
     const char* __restrict__ ws, const typename E::storage* __restrict__ v,
@@ -566,37 +586,37 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
   using M = typename S::M;
   using frag = typename S::frag;
   using St = typename E::storage;
+  constexpr int SPW = K::SPW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int chain = blockIdx.x, vb = blockIdx.y;
   const int b = chain / H, h = chain - b * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool copier = wave == K::NC;
+  const bool copier = wave >= K::NCW && wave < K::NCW + K::NCP;
+  const bool storer = wave == K::NCW + K::NCP;
+  const int cw = wave - K::NCW;  // copy-wave index
   const long rs = static_cast<long>(H) * DV;  // element stride between tokens
   const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
 
-  // ------------------------------------------------------------ copy wave
-  // Lane map of a value/output tile row: lane l covers row (l / LPR) of the
-  // instruction's RPI rows, bytes 16 * (l % LPR) of it.
+  // ------------------------------------------------------------ copy waves
   const int crow = lane / K::LPR, cbyte = 16 * (lane % K::LPR);
   auto stage_slot = [&](int n, int buf) {
     const char* src = ws + (static_cast<long>(chain) * nchunk + n) * K::SLOT;
     char* dst = lds + buf * K::SLOT;
-    for (int u = 0; u < K::SLOT / 1024; ++u)
+    for (int u = cw; u < K::SLOT / 1024; u += K::NCP)
       __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)(dst + u * 1024), 16, 0, 0);
   };
   auto stage_v = [&](int n) {
     char* dst = lds + K::OFF_V + (n & 1) * K::VTILE;
-#pragma unroll
-    for (int u = 0; u < K::NVI; ++u) {
+    for (int u = cw; u < K::NVI; u += K::NCP) {
       const int t = min(n * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
       const char* src = reinterpret_cast<const char*>(v + base + t * rs) + cbyte;
       __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
     }
   };
+  // Output tile of chunk n: LDS rows straight to 16-byte global stores.
   auto store_out = [&](int n) {
     const char* src = lds + K::OFF_O + (n & 1) * K::VTILE;
-#pragma unroll
     for (int u = 0; u < K::NVI; ++u) {
       const int r = u * K::RPI + crow, t = n * C + r;
       const uint4 x = *reinterpret_cast<const uint4*>(src + u * 1024 + lane * 16);
@@ -606,95 +626,113 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
 
   // --------------------------------------------------------- compute waves
   const int c16 = lane & 15, g = lane >> 4;
-  const int lcol = 16 * wave + c16;  // column inside the value block
-  const int col = vb * DVB + lcol;
-  f32x4 Sa[S::NTK];  // Sa[ti] holds S[16 ti + 4 g + e][col]
-  if (!copier) {
-    if (S0 != nullptr) {
-      const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+  // Sa[j][ti] holds S[16 ti + 4 g + e][col(j)], col(j) = 16 (wave * SPW + j) + c16.
+  f32x4 Sa[SPW][S::NTK];
+  if (!copier && !storer) {
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti)
+    for (int j = 0; j < SPW; ++j) {
+      const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
+      if (S0 != nullptr) {
+        const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sa[ti][e] = s0[(16 * ti + e) * DV];
-    } else {
+        for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int e = 0; e < 4; ++e) Sa[j][ti][e] = s0[(16 * ti + e) * DV];
+      } else {
+#pragma unroll
+        for (int ti = 0; ti < S::NTK; ++ti) Sa[j][ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-  } else if (nchunk > 0) {
+  } else if (copier && nchunk > 0) {
     stage_slot(0, 0);
     stage_v(0);
     __builtin_amdgcn_s_waitcnt(0);
   }
 
   for (int n = 0; n < nchunk; ++n) {
-    __syncthreads();  // slot n and values n are in LDS; output n-1 is in LDS
-    if (copier) {
-      if (n > 0) store_out(n - 1);
+    const int t0 = n * C;
+    // [A].  The store wave passes it without draining its global stores:
+    // nothing in the workgroup waits on them.
+    if (storer)
+      __builtin_amdgcn_s_barrier();
+    else
+      __syncthreads();
+    if (storer) {
+      if (n > 0) store_out(n - 1);  // its LDS reads complete before the stores issue
+    } else if (copier) {
       if (n + 1 < nchunk) {
         if (K::NBUF == 2) stage_slot(n + 1, (n + 1) & 1);
         stage_v(n + 1);
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      if (K::NBUF == 2) __builtin_amdgcn_s_waitcnt(0);
     } else {
-      const int t0 = n * C;
+      f32x4 R[SPW][S::NT];
+      const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tr + 4 * g + e;
+            const float x = load_scalar(vt, r * DVB + 16 * (wave * SPW + j) + c16);
+            R[j][tr][e] = t0 + r < T ? x : 0.f;
+          }
       const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
       auto fr = [&](int off, int idx) -> frag {
         return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
       };
       const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
-      const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
       St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-      f32x4 R[S::NT];
+      frag sfr[SPW][S::NKS];
 #pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr)
+      for (int j = 0; j < SPW; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tr + 4 * g + e;
-          const float x = load_scalar(vt, r * DVB + lcol);
-          R[tr][e] = t0 + r < T ? x : 0.f;
-        }
-      frag sfr[S::NKS];
-#pragma unroll
-      for (int s2 = 0; s2 < S::NKS; ++s2) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        sfr[s2] = M::from_acc(Sa[2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[2 * s2 + 1]);
-      }
+        for (int s2 = 0; s2 < S::NKS; ++s2)
+          sfr[j][s2] = M::from_acc(Sa[j][2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[j][2 * s2 + 1]);
       // R = V - K+ S
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr) {
         frag a[S::NKS];
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_KP, tr * S::NKS + s2);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[s2], acc);
-        R[tr] -= acc;
-      }
-      frag rfr[S::NCS];
+        for (int j = 0; j < SPW; ++j) {
+          f32x4 acc = z;
 #pragma unroll
-      for (int s2 = 0; s2 < S::NCS; ++s2) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        rfr[s2] = M::from_acc(R[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[2 * s2 + 1]);
+          for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[j][s2], acc);
+          R[j][tr] -= acc;
+        }
       }
+      frag rfr[SPW][S::NCS];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int s2 = 0; s2 < S::NCS; ++s2)
+          rfr[j][s2] = M::from_acc(R[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[j][2 * s2 + 1]);
       // U = Tm R  (Tm lower triangular: k-steps up to the diagonal tile)
-      f32x4 U[S::NT];
+      f32x4 U[SPW][S::NT];
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr) {
         frag a[S::NCS];
 #pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) a[s2] = fr(S::OFF_TM, tr * S::NCS + s2);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 <= tr / 2; ++s2) a[s2] = fr(S::OFF_TM, S::tri(tr) + s2);
 #pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(a[s2], rfr[s2], acc);
-        U[tr] = acc;
-      }
-      frag ufr[S::NCS];
+        for (int j = 0; j < SPW; ++j) {
+          f32x4 acc = z;
 #pragma unroll
-      for (int s2 = 0; s2 < S::NCS; ++s2) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        ufr[s2] = M::from_acc(U[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[2 * s2 + 1]);
+          for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(a[s2], rfr[j][s2], acc);
+          U[j][tr] = acc;
+        }
       }
+      frag ufr[SPW][S::NCS];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int s2 = 0; s2 < S::NCS; ++s2)
+          ufr[j][s2] = M::from_acc(U[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[j][2 * s2 + 1]);
       // O = Q+ S + P U, into the output tile
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr) {
@@ -702,14 +740,18 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_QP, tr * S::NKS + s2);
 #pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) p[s2] = fr(S::OFF_PP, tr * S::NCS + s2);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 <= tr / 2; ++s2) p[s2] = fr(S::OFF_PP, S::tri(tr) + s2);
 #pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[s2], acc);
+        for (int j = 0; j < SPW; ++j) {
+          f32x4 acc = z;
 #pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(p[s2], ufr[s2], acc);
+          for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[j][s2], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_scalar(ot, (16 * tr + 4 * g + e) * DVB + lcol, acc[e]);
+          for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(p[s2], ufr[j][s2], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16, acc[e]);
+        }
       }
       // S <- Diag(gamma_C) S + Kbar^T U
 #pragma unroll
@@ -717,51 +759,62 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
         frag a[S::NCS];
 #pragma unroll
         for (int s2 = 0; s2 < S::NCS; ++s2) a[s2] = fr(S::OFF_KB, ti * S::NCS + s2);
-        f32x4 acc = Sa[ti];
         const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
-        acc *= gc;
 #pragma unroll
-        for (int s2 = 0; s2 < S::NCS; ++s2) acc = M::mma(a[s2], ufr[s2], acc);
-        Sa[ti] = acc;
+        for (int j = 0; j < SPW; ++j) {
+          f32x4 acc = Sa[j][ti] * gc;
+#pragma unroll
+          for (int s2 = 0; s2 < S::NCS; ++s2) acc = M::mma(a[s2], ufr[j][s2], acc);
+          Sa[j][ti] = acc;
+        }
       }
     }
-    if (K::NBUF == 1 && n + 1 < nchunk) {
-      __syncthreads();  // every compute wave is done with the single slot
+    if (K::NBUF == 1) {
+      if (storer)
+        __builtin_amdgcn_s_barrier();
+      else
+        __syncthreads();  // every compute wave is done with the single slot
       if (copier) {
-        stage_slot(n + 1, 0);
+        if (n + 1 < nchunk) stage_slot(n + 1, 0);
         __builtin_amdgcn_s_waitcnt(0);
       }
     }
   }
   if (nchunk > 0) {
-    __syncthreads();  // the last output tile is in LDS
-    if (copier) store_out(nchunk - 1);
+    if (storer)
+      __builtin_amdgcn_s_barrier();
+    else
+      __syncthreads();  // the last output tile is in LDS
+    if (storer) store_out(nchunk - 1);
   }
+  if (storer) __builtin_amdgcn_s_waitcnt(0);
 
-  if (!copier && ST != nullptr) {
-    float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+  if (!copier && !storer && ST != nullptr) {
 #pragma unroll
-    for (int ti = 0; ti < S::NTK; ++ti)
+    for (int j = 0; j < SPW; ++j) {
+      const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
+      float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
+      for (int ti = 0; ti < S::NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[j][ti][e];
+    }
   }
 }
 
 // ================================================================== host
 
-// Value-block width of a state-pass workgroup: two 16-column slabs (one wave
-// each), or all of d_v when it is 16.
+template <typename E, int DK, int C>
+constexpr bool prep_fits() { return sizeof(typename PrepCfg<E, DK, C>::Smem) <= kLdsLimit / 2; }
+
+// Value-block width of a state-pass workgroup: 32 columns (two compute
+// waves), or 16 when d_v is 16.
 constexpr int dvb_for(int dv) { return dv < 32 ? dv : 32; }
 
-template <typename E, int DK, int C>
+template <typename E, int DK, int DV, int C>
 constexpr bool fits() {
-  return sizeof(typename PrepCfg<E, DK, C>::Smem) <= kLdsLimit / 2 &&
-         PassCfg<E, DK, 32, C>::smem_bytes <= kLdsLimit &&
-         PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit;
+  return prep_fits<E, DK, C>() && PassCfg<E, DK, dvb_for(DV), C>::smem_bytes <= kLdsLimit;
 }
-
-template <typename E, int DK, int C>
-size_t slot_bytes() { return Shape<E, DK, C>::SLOT; }
 
 int g_num_cus = 0;
 int num_cus() {
@@ -776,10 +829,11 @@ int num_cus() {
   return g_num_cus;
 }
 
-template <typename E, int DK, int C>
+template <typename E, int DK, int DV, int C>
 hipError_t launch_t(const PrefillArgs& a) {
   using St = typename E::storage;
-  using S = Shape<E, DK, C>;
+  constexpr int DVB = dvb_for(DV);
+  using K = PassCfg<E, DK, DVB, C>;
   const int nchunk = (a.T + C - 1) / C;
   const long ntask = static_cast<long>(a.B) * a.H * nchunk;
   char* ws = static_cast<char*>(a.workspace);
@@ -793,42 +847,49 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  auto pass = [&](auto dvb_tag) -> hipError_t {
-    constexpr int DVB = decltype(dvb_tag)::value;
-    using K = PassCfg<E, DK, DVB, C>;
-    static bool attr_set = false;  // one-time opt-in to more than 64 KiB of LDS
-    if (!attr_set) {
-      const void* fn = reinterpret_cast<const void*>(&state_pass_kernel<E, DK, DVB, C>);
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         static_cast<int>(K::smem_bytes));
-      if (e != hipSuccess) return e;
-      attr_set = true;
+  static bool attr_set = false;  // one-time opt-in to more than 64 KiB of LDS
+  if (!attr_set) {
+    const void* fn = reinterpret_cast<const void*>(&state_pass_kernel<E, DK, DVB, C>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(K::smem_bytes));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // grid.x = (batch, head) chains, grid.y = value blocks: the value blocks
+  // of one chain are gridDim.x apart in dispatch order, which keeps them on
+  // one XCD (and its L2) whenever gridDim.x is a multiple of 8.
+  hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, DV / DVB),
+                     dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
+                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, DV, nchunk);
+  return hipGetLastError();
+}
+
+template <typename E, int DK, int C>
+hipError_t dispatch_dv(const PrefillArgs& a, size_t* slot) {
+  switch (a.d_v) {
+#define KDA_CASE(DV)                                                            \
+  case DV:                                                                      \
+    if constexpr (fits<E, DK, DV, C>()) {                                       \
+      if (slot) { *slot = Shape<E, DK, C>::SLOT; return hipSuccess; }           \
+      return launch_t<E, DK, DV, C>(a);                                         \
+    } else {                                                                    \
+      return hipErrorNotSupported;                                              \
     }
-    hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, a.d_v / DVB),
-                       dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
-                       a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, a.d_v, nchunk);
-    return hipGetLastError();
-  };
-  (void)sizeof(S);
-  if (a.d_v == 16) return pass(std::integral_constant<int, 16>{});
-  return pass(std::integral_constant<int, 32>{});
+    KDA_CASE(16)
+    KDA_CASE(32)
+    KDA_CASE(64)
+    KDA_CASE(128)
+#undef KDA_CASE
+  }
+  return hipErrorNotSupported;
 }
 
 template <typename E, int DK>
 hipError_t dispatch_c(const PrefillArgs& a, size_t* slot) {
   switch (a.chunk) {
-#define KDA_CASE(CC)                                                      \
-  case CC:                                                                \
-    if constexpr (fits<E, DK, CC>()) {                                    \
-      if (slot) { *slot = slot_bytes<E, DK, CC>(); return hipSuccess; }   \
-      return launch_t<E, DK, CC>(a);                                      \
-    } else {                                                              \
-      return hipErrorNotSupported;                                        \
-    }
-    KDA_CASE(16)
-    KDA_CASE(32)
-    KDA_CASE(64)
-#undef KDA_CASE
+    case 16: return dispatch_dv<E, DK, 16>(a, slot);
+    case 32: return dispatch_dv<E, DK, 32>(a, slot);
+    case 64: return dispatch_dv<E, DK, 64>(a, slot);
   }
   return hipErrorNotSupported;
 }

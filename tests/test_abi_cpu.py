@@ -34,7 +34,7 @@ def test_version_and_status_strings():
 def test_workspace_query():
     ws = kda.lib().kda_fwd_chunked_workspace_bytes
     one = ws(1, 64, 1, 128, 128, 64, kda.KDA_BF16)      # one chunk's slot
-    assert one % 1024 == 0 and 64 * 1024 <= one <= 66 * 1024
+    assert one % 1024 == 0 and 60 * 1024 <= one <= 66 * 1024
     assert ws(4, 16384, 16, 128, 128, 64, kda.KDA_BF16) == 4 * 16 * 256 * one
     assert ws(1, 65, 1, 128, 128, 64, kda.KDA_BF16) == 2 * one   # ragged tail: one more slot
     assert ws(1, 0, 1, 128, 128, 64, kda.KDA_BF16) == 0
