@@ -176,7 +176,8 @@ def bench_decode(steps: int, warmup: int):
 
 def cpu_baseline(sample_tokens: int):
     """Time the fp64 oracle on the first `sample_tokens` positions of every
-    (batch, head) chain of the prefill workload, on the host cores."""
+    (batch, head) chain of the prefill workload on all host cores, and on one
+    chain with a single thread."""
     import oracle
     from synth import WORKLOADS, workload_inputs
 
@@ -186,10 +187,18 @@ def cpu_baseline(sample_tokens: int):
     t0 = time.perf_counter()
     oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"], threads=threads)
     dt = time.perf_counter() - t0
+    # one (batch, head) chain, one thread: per token-head rate
+    one = {n: x[n][:1, :, :1] for n in ("q", "k", "v", "alpha", "beta")}
+    t1 = time.perf_counter()
+    oracle.kda_forward(one["q"], one["k"], one["v"], one["alpha"], one["beta"], x["S0"][:1, :1],
+                       threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": w.B * sample_tokens / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{PREFILL}: all {w.B * w.H} (batch, head) chains, first {sample_tokens} "
-                      f"of {w.T} tokens, fp64 token recurrence, {dt:.2f} s wall"}
+                      f"of {w.T} tokens, fp64 token recurrence, {dt:.2f} s wall on {threads} "
+                      f"threads",
+            "single_thread_token_heads_per_s": round(sample_tokens / dt1, 1)}
 
 
 def profile_pass():
@@ -218,7 +227,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--long-steps", type=int, default=5)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -252,6 +261,7 @@ def main():
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": _recorded_traffic("kda_prefill.hip", "prefill_b4_h16_t16k_counters.txt"),
                 "alg_bytes_per_launch": by, "launch_ms": round(launch_ms, 4),
+                "launch": "one kda_fwd_chunked call: chunk_prep_kernel + state_pass_kernel",
                 "mfma": {"achieved_tflops": round(tfl, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                          "frac": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4), "alg_flops_per_launch": fl}}
 
@@ -269,7 +279,8 @@ def main():
                            "unit": "GB/s", "frac": round(d_gbs / HBM_PEAK_GBS, 4),
                            "traffic": _recorded_traffic("kda_decode.hip",
                                                         "decode_b256_h16_counters.txt"),
-                           "alg_bytes_per_launch": dby, "launch_ms": round(d_launch, 4)}}
+                           "alg_bytes_per_launch": dby, "launch_ms": round(d_launch, 4),
+                           "launch": "one kda_decode_step call: decode_kernel"}}
 
     long_ctx = None
     if not args.no_long:
