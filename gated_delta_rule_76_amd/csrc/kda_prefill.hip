@@ -51,6 +51,7 @@ namespace kda {
 namespace {
 
 typedef __attribute__((address_space(1))) void gvoid_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lvoid_t;
 
 // ----------------------------------------------------------------- helpers
@@ -243,8 +244,12 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   const int ch0 = 8 * cg;
 
   // Token row of (task, r), clamped into the sequence so loads stay in bounds.
+  // Tasks are chunk-major (task = n * nchain + chain), so the workspace holds
+  // chunk n of every chain in one contiguous run, which the state pass reads
+  // at its step n.
+  const int nchain = ntask / nchunk;
   auto rowptr = [&](int task, int r) -> long {
-    const int chain = task / nchunk, n = task - chain * nchunk;
+    const int n = task / nchain, chain = task - n * nchain;
     const int b = chain / H, h = chain - b * H;
     const int t = min(n * C + r, T - 1);
     return (static_cast<long>(b) * T + t) * H + h;
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   prefetch(blockIdx.x);
 
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int n = task % nchunk;
+    const int n = task / nchain;
     const int valid = min(C, T - n * C);
     char* slot = ws + static_cast<long>(task) * S::SLOT;
 
@@ -544,8 +549,11 @@ struct PassCfg {
   static constexpr int NSLAB = DVB / 16;                 // 16-column state slabs
   static constexpr int NCW = NSLAB < 4 ? NSLAB : 4;      // compute waves
   static constexpr int SPW = NSLAB / NCW;                // slabs per compute wave
-  static constexpr int NCP = 6;                          // copy waves (loads)
+  static constexpr int NCP = 8;                          // copy waves (loads)
   static constexpr int NTH = 64 * (NCW + NCP + 1);       // + one store wave
+  // One workgroup per CU: its waves spread over the 4 SIMDs, so a SIMD holds
+  // WPE of them and each may use 512 / WPE registers.
+  static constexpr int WPE = (NTH / 64 + 3) / 4;
   static constexpr int SLOT = S::SLOT;
   static constexpr int ESZ = static_cast<int>(sizeof(typename E::storage));
   // Value / output tiles of one chunk: C rows x DVB columns, row-major,
@@ -577,7 +585,8 @@ struct PassCfg {
 //          on inside the loop; drained once before the wave ends)
 //   compute: values n into registers, the five products, output n into LDS
 template <typename E, int DK, int DVB, int C>
-__global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kernel(
+__global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH))
+__attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, DVB, C>::WPE))) void state_pass_kernel(
     const char* __restrict__ ws, const typename E::storage* __restrict__ v,
     const float* __restrict__ S0, typename E::storage* __restrict__ o, float* __restrict__ ST,
     int T, int H, int DV, int nchunk) {
@@ -601,7 +610,7 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
   // ------------------------------------------------------------ copy waves
   const int crow = lane / K::LPR, cbyte = 16 * (lane % K::LPR);
   auto stage_slot = [&](int n, int buf) {
-    const char* src = ws + (static_cast<long>(chain) * nchunk + n) * K::SLOT;
+    const char* src = ws + (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
     char* dst = lds + buf * K::SLOT;
     for (int u = cw; u < K::SLOT / 1024; u += K::NCP)
       __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)(dst + u * 1024), 16, 0, 0);
@@ -614,13 +623,25 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
       __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
     }
   };
-  // Output tile of chunk n: LDS rows straight to 16-byte global stores.
+  // The compiler makes any LDS read wait for every earlier global access of
+  // the wave (it cannot tell this wave's stores from the copy waves' LDS-DMA
+  // loads), which would hold this wave at each chunk until the previous
+  // chunk's stores are acknowledged.  The reads are therefore written out
+  // with their own LDS wait; the data was published by the barrier before.
   auto store_out = [&](int n) {
-    const char* src = lds + K::OFF_O + (n & 1) * K::VTILE;
+    const uint32_t src = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) char*)(lds + K::OFF_O + (n & 1) * K::VTILE + lane * 16)));
+    uint4 x[K::NVI];
+#pragma unroll
+    for (int u = 0; u < K::NVI; ++u) {
+      u32x4 y;
+      asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(y) : "v"(src), "i"(u * 1024) : "memory");
+      x[u] = uint4{y[0], y[1], y[2], y[3]};
+    }
+#pragma unroll
     for (int u = 0; u < K::NVI; ++u) {
       const int r = u * K::RPI + crow, t = n * C + r;
-      const uint4 x = *reinterpret_cast<const uint4*>(src + u * 1024 + lane * 16);
-      if (r < C && t < T) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x;
+      if (r < C && t < T) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x[u];
     }
   };
 
@@ -666,108 +687,137 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH)) void state_pass_kern
       }
       if (K::NBUF == 2) __builtin_amdgcn_s_waitcnt(0);
     } else {
-      f32x4 R[SPW][S::NT];
+      // Each product first issues all of its LDS operand reads, then runs its
+      // MFMAs with the independent accumulator chains interleaved (k-step
+      // outermost), so the matrix pipe is not waiting on one chain.
+      const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
+      auto fr = [&](int off, int idx) -> frag {
+        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
+      };
       const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
+      St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
+      const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+      frag akp[S::NT][S::NKS];
+#pragma unroll
+      for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+        for (int s2 = 0; s2 < S::NKS; ++s2) akp[tr][s2] = fr(S::OFF_KP, tr * S::NKS + s2);
+      float vr[SPW][S::NT][4];
 #pragma unroll
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * tr + 4 * g + e;
-            const float x = load_scalar(vt, r * DVB + 16 * (wave * SPW + j) + c16);
-            R[j][tr][e] = t0 + r < T ? x : 0.f;
-          }
-      const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
-      auto fr = [&](int off, int idx) -> frag {
-        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
-      };
-      const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
-      St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-
+          for (int e = 0; e < 4; ++e)
+            vr[j][tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16);
       frag sfr[SPW][S::NKS];
 #pragma unroll
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2)
           sfr[j][s2] = M::from_acc(Sa[j][2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[j][2 * s2 + 1]);
+
       // R = V - K+ S
+      f32x4 R[SPW][S::NT];
 #pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr) {
-        frag a[S::NKS];
+      for (int j = 0; j < SPW; ++j)
 #pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_KP, tr * S::NKS + s2);
+        for (int tr = 0; tr < S::NT; ++tr) R[j][tr] = z;
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          f32x4 acc = z;
+      for (int s2 = 0; s2 < S::NKS; ++s2)
 #pragma unroll
-          for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[j][s2], acc);
-          R[j][tr] -= acc;
-        }
-      }
+        for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) R[j][tr] = M::mma(akp[tr][s2], sfr[j][s2], R[j][tr]);
+      frag atm[S::NTRI];
+#pragma unroll
+      for (int i = 0; i < S::NTRI; ++i) atm[i] = fr(S::OFF_TM, i);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            R[j][tr][e] = (t0 + 16 * tr + 4 * g + e < T ? vr[j][tr][e] : 0.f) - R[j][tr][e];
       frag rfr[SPW][S::NCS];
 #pragma unroll
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int s2 = 0; s2 < S::NCS; ++s2)
           rfr[j][s2] = M::from_acc(R[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[j][2 * s2 + 1]);
-      // U = Tm R  (Tm lower triangular: k-steps up to the diagonal tile)
+
+      // U = Tm R  (Tm lower triangular: row tile tr uses k-steps s2 <= tr / 2)
       f32x4 U[SPW][S::NT];
 #pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr) {
-        frag a[S::NCS];
+      for (int j = 0; j < SPW; ++j)
 #pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) a[s2] = fr(S::OFF_TM, S::tri(tr) + s2);
+        for (int tr = 0; tr < S::NT; ++tr) U[j][tr] = z;
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          f32x4 acc = z;
+      for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
-          for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(a[s2], rfr[j][s2], acc);
-          U[j][tr] = acc;
-        }
-      }
+        for (int tr = 2 * s2; tr < S::NT; ++tr)
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) U[j][tr] = M::mma(atm[S::tri(tr) + s2], rfr[j][s2], U[j][tr]);
+      frag akb[S::NTK][S::NCS];
+#pragma unroll
+      for (int ti = 0; ti < S::NTK; ++ti)
+#pragma unroll
+        for (int s2 = 0; s2 < S::NCS; ++s2) akb[ti][s2] = fr(S::OFF_KB, ti * S::NCS + s2);
       frag ufr[SPW][S::NCS];
 #pragma unroll
       for (int j = 0; j < SPW; ++j)
 #pragma unroll
         for (int s2 = 0; s2 < S::NCS; ++s2)
           ufr[j][s2] = M::from_acc(U[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[j][2 * s2 + 1]);
-      // O = Q+ S + P U, into the output tile
-#pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr) {
-        frag a[S::NKS], p[S::NCS];
-#pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2) a[s2] = fr(S::OFF_QP, tr * S::NKS + s2);
-#pragma unroll
-        for (int s2 = 0; s2 <= tr / 2; ++s2) p[s2] = fr(S::OFF_PP, S::tri(tr) + s2);
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          f32x4 acc = z;
-#pragma unroll
-          for (int s2 = 0; s2 < S::NKS; ++s2) acc = M::mma(a[s2], sfr[j][s2], acc);
-#pragma unroll
-          for (int s2 = 0; s2 <= tr / 2; ++s2) acc = M::mma(p[s2], ufr[j][s2], acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16, acc[e]);
-        }
-      }
+
       // S <- Diag(gamma_C) S + Kbar^T U
 #pragma unroll
       for (int ti = 0; ti < S::NTK; ++ti) {
-        frag a[S::NCS];
-#pragma unroll
-        for (int s2 = 0; s2 < S::NCS; ++s2) a[s2] = fr(S::OFF_KB, ti * S::NCS + s2);
         const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-          f32x4 acc = Sa[j][ti] * gc;
-#pragma unroll
-          for (int s2 = 0; s2 < S::NCS; ++s2) acc = M::mma(a[s2], ufr[j][s2], acc);
-          Sa[j][ti] = acc;
-        }
+        for (int j = 0; j < SPW; ++j) Sa[j][ti] *= gc;
       }
+#pragma unroll
+      for (int s2 = 0; s2 < S::NCS; ++s2)
+#pragma unroll
+        for (int ti = 0; ti < S::NTK; ++ti)
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) Sa[j][ti] = M::mma(akb[ti][s2], ufr[j][s2], Sa[j][ti]);
+
+      // O = Q+ S_in + P U  (S_in is still held as the bf16 operand sfr)
+      frag aqp[S::NT][S::NKS], app[S::NTRI];
+#pragma unroll
+      for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+        for (int s2 = 0; s2 < S::NKS; ++s2) aqp[tr][s2] = fr(S::OFF_QP, tr * S::NKS + s2);
+#pragma unroll
+      for (int i = 0; i < S::NTRI; ++i) app[i] = fr(S::OFF_PP, i);
+      f32x4 O[SPW][S::NT];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr) O[j][tr] = z;
+#pragma unroll
+      for (int s2 = 0; s2 < S::NKS; ++s2)
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) O[j][tr] = M::mma(aqp[tr][s2], sfr[j][s2], O[j][tr]);
+#pragma unroll
+      for (int s2 = 0; s2 < S::NCS; ++s2)
+#pragma unroll
+        for (int tr = 2 * s2; tr < S::NT; ++tr)
+#pragma unroll
+          for (int j = 0; j < SPW; ++j) O[j][tr] = M::mma(app[S::tri(tr) + s2], ufr[j][s2], O[j][tr]);
+#pragma unroll
+      for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16, O[j][tr][e]);
     }
     if (K::NBUF == 1) {
       if (storer)
