@@ -549,8 +549,8 @@ struct PassCfg {
   static constexpr int NSLAB = DVB / 16;                 // 16-column state slabs
   static constexpr int NCW = NSLAB < 4 ? NSLAB : 4;      // compute waves
   static constexpr int SPW = NSLAB / NCW;                // slabs per compute wave
-  static constexpr int NCP = 8;                          // copy waves (loads)
-  static constexpr int NTH = 64 * (NCW + NCP + 1);       // + one store wave
+  static constexpr int NCP = 10 - NCW;                   // copy waves (loads): 11 waves in all
+  static constexpr int NTH = 64 * (NCW + NCP + 2);       // + one store wave, one prefetch wave
   // One workgroup per CU: its waves spread over the 4 SIMDs, so a SIMD holds
   // WPE of them and each may use 512 / WPE registers.
   static constexpr int WPE = (NTH / 64 + 3) / 4;
@@ -571,7 +571,8 @@ struct PassCfg {
       2 * static_cast<size_t>(SLOT) + 4 * static_cast<size_t>(VTILE) <= kLdsLimit ? 2 : 1;
   static constexpr int OFF_V = NBUF * SLOT;
   static constexpr int OFF_O = OFF_V + 2 * VTILE;
-  static constexpr size_t smem_bytes = static_cast<size_t>(OFF_O) + 2 * VTILE;
+  static constexpr int OFF_SINK = OFF_O + 2 * VTILE;      // 1 KiB the prefetch loads land in
+  static constexpr size_t smem_bytes = static_cast<size_t>(OFF_SINK) + 1024;
 };
 
 // One workgroup per (batch, head, block of DVB value columns).  Compute
@@ -603,6 +604,8 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool copier = wave >= K::NCW && wave < K::NCW + K::NCP;
   const bool storer = wave == K::NCW + K::NCP;
+  const bool fetcher = wave == K::NCW + K::NCP + 1;
+  const bool computer = wave < K::NCW;
   const int cw = wave - K::NCW;  // copy-wave index
   const long rs = static_cast<long>(H) * DV;  // element stride between tokens
   const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
@@ -621,6 +624,24 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       const int t = min(n * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
       const char* src = reinterpret_cast<const char*>(v + base + t * rs) + cbyte;
       __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
+    }
+  };
+  // Prefetch wave: pulls its share of chunk n's slot (the value blocks of a
+  // chain split the slot units between them) and its own value rows into
+  // L2, so that the copy waves' loads for that chunk hit there.  Each load is
+  // a whole 1 KiB unit (partial-line touches do not fill the line); the data
+  // lands in a 1 KiB LDS sink that is never read.
+  const int qu = (K::SLOT / 1024 + gridDim.y - 1) / gridDim.y;
+  auto prefetch = [&](int n) {
+    const char* src = ws + (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
+    char* sink = lds + K::OFF_SINK;
+    for (int i = 0; i < qu; ++i) {
+      const int u = min(vb * qu + i, K::SLOT / 1024 - 1);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)sink, 16, 0, 0);
+    }
+    for (int u = 0; u < K::NVI; ++u) {
+      const int t = min(n * C + u * K::RPI + crow, T - 1);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(reinterpret_cast<const char*>(v + base + t * rs) + cbyte), (lvoid_t*)sink, 16, 0, 0);
     }
   };
   // The compiler makes any LDS read wait for every earlier global access of
@@ -649,7 +670,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   const int c16 = lane & 15, g = lane >> 4;
   // Sa[j][ti] holds S[16 ti + 4 g + e][col(j)], col(j) = 16 (wave * SPW + j) + c16.
   f32x4 Sa[SPW][S::NTK];
-  if (!copier && !storer) {
+  if (computer) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
@@ -668,18 +689,25 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     stage_slot(0, 0);
     stage_v(0);
     __builtin_amdgcn_s_waitcnt(0);
+  } else if (fetcher && nchunk > 1) {
+    prefetch(1);
   }
 
   for (int n = 0; n < nchunk; ++n) {
     const int t0 = n * C;
     // [A].  The store wave passes it without draining its global stores:
     // nothing in the workgroup waits on them.
-    if (storer)
+    if (storer || fetcher)
       __builtin_amdgcn_s_barrier();
     else
       __syncthreads();
     if (storer) {
       if (n > 0) store_out(n - 1);  // its LDS reads complete before the stores issue
+    } else if (fetcher) {
+      if (n + 2 < nchunk) {
+        __builtin_amdgcn_s_waitcnt(0);  // the previous chunk's prefetch has landed
+        prefetch(n + 2);
+      }
     } else if (copier) {
       if (n + 1 < nchunk) {
         if (K::NBUF == 2) stage_slot(n + 1, (n + 1) & 1);
@@ -820,7 +848,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
             store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16, O[j][tr][e]);
     }
     if (K::NBUF == 1) {
-      if (storer)
+      if (storer || fetcher)
         __builtin_amdgcn_s_barrier();
       else
         __syncthreads();  // every compute wave is done with the single slot
@@ -831,15 +859,15 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     }
   }
   if (nchunk > 0) {
-    if (storer)
+    if (storer || fetcher)
       __builtin_amdgcn_s_barrier();
     else
       __syncthreads();  // the last output tile is in LDS
     if (storer) store_out(nchunk - 1);
   }
-  if (storer) __builtin_amdgcn_s_waitcnt(0);
+  if (storer || fetcher) __builtin_amdgcn_s_waitcnt(0);
 
-  if (!copier && !storer && ST != nullptr) {
+  if (computer && ST != nullptr) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
