@@ -547,9 +547,11 @@ template <typename E, int DK, int DVB, int C>
 struct PassCfg {
   using S = Shape<E, DK, C>;
   static constexpr int NSLAB = DVB / 16;                 // 16-column state slabs
-  static constexpr int NCW = NSLAB < 4 ? NSLAB : 4;      // compute waves
-  static constexpr int SPW = NSLAB / NCW;                // slabs per compute wave
-  static constexpr int NCP = 10 - NCW;                   // copy waves (loads): 11 waves in all
+  // Two compute waves per slab: the state wave runs the sequential chain
+  // (K+ S, Tm R, Kbar^T U) and hands the bf16 state and U to the output wave,
+  // which forms O = Q+ S + P U next to it on another SIMD.
+  static constexpr int NCW = 2 * NSLAB;
+  static constexpr int NCP = 10 - NCW;                   // copy waves (loads)
   static constexpr int NTH = 64 * (NCW + NCP + 2);       // + one store wave, one prefetch wave
   // One workgroup per CU: its waves spread over the 4 SIMDs, so a SIMD holds
   // WPE of them and each may use 512 / WPE registers.
@@ -564,27 +566,41 @@ struct PassCfg {
   static constexpr int RPI = 64 / LPR;                   // rows per wave instruction
   static constexpr int NVI = (C + RPI - 1) / RPI;        // instructions per tile
   static constexpr int VTILE = NVI * 1024;               // bytes per tile buffer
-  static_assert(VROW % 16 == 0 && 64 % LPR == 0 && NSLAB % NCW == 0, "pass map");
-  // Double-buffer the slot when two fit next to the (double-buffered)
-  // value and output tiles.
-  static constexpr int NBUF =
-      2 * static_cast<size_t>(SLOT) + 4 * static_cast<size_t>(VTILE) <= kLdsLimit ? 2 : 1;
+  static_assert(VROW % 16 == 0 && 64 % LPR == 0 && NSLAB <= 2, "pass map");
+  // Hand-over areas: the state operand S (NKS fragments per slab, double
+  // buffered: written at the end of chunk n for chunk n + 1), U (NCS
+  // fragments per slab) and one ready counter per slab.
+  static constexpr int XS = NSLAB * S::NKS * S::FRAG;
+  static constexpr int XU = NSLAB * S::NCS * S::FRAG;
+  static constexpr int REST = 4 * VTILE + 1024 + 2 * XS + XU + 64;
+  // Double-buffer the slot when two fit next to everything else.
+  static constexpr int NBUF = 2 * static_cast<size_t>(SLOT) + REST <= kLdsLimit ? 2 : 1;
   static constexpr int OFF_V = NBUF * SLOT;
   static constexpr int OFF_O = OFF_V + 2 * VTILE;
-  static constexpr int OFF_SINK = OFF_O + 2 * VTILE;      // 1 KiB the prefetch loads land in
-  static constexpr size_t smem_bytes = static_cast<size_t>(OFF_SINK) + 1024;
+  static constexpr int OFF_SINK = OFF_O + 2 * VTILE;     // 1 KiB the prefetch loads land in
+  static constexpr int OFF_XS = OFF_SINK + 1024;
+  static constexpr int OFF_XU = OFF_XS + 2 * XS;
+  static constexpr int OFF_FLAG = OFF_XU + XU;
+  static constexpr size_t smem_bytes = static_cast<size_t>(OFF_FLAG) + 64;
 };
 
-// One workgroup per (batch, head, block of DVB value columns).  Compute
-// waves own SPW 16-column slabs of the fp32 state each; copy waves move the
-// workspace slot and the value tile into LDS; a store wave writes the output
-// tile out of it.  Value and output tiles are double-buffered, the slot too
-// when it fits, so one barrier per chunk suffices:
-//   [A] slot n and values n are in LDS, output n-1 is complete in LDS
+// One workgroup per (batch, head, block of DVB value columns).  Each
+// 16-column slab of the fp32 state has a state wave, which keeps the slab in
+// accumulator registers and runs the sequential chain, and an output wave on
+// another SIMD, which forms the slab's output from the state and U the state
+// wave hands over in LDS.  Copy waves move the workspace slot and the value
+// tile into LDS, a store wave writes the output tile out of it, and a
+// prefetch wave pulls later slots into L2.  Value and output tiles are
+// double-buffered, the slot too when it fits, so one barrier per chunk
+// suffices:
+//   [A] slot n and values n are in LDS, output n-1 is complete in LDS, the
+//       state operand entering chunk n is in its hand-over buffer
 //   copy: start slot n+1 and values n+1, wait for them
 //   store: read output n-1 from LDS, issue its global stores (never waited
 //          on inside the loop; drained once before the wave ends)
-//   compute: values n into registers, the five products, output n into LDS
+//   state: R = V - K+ S, U = Tm R, publish U, S <- gamma_C S + Kbar^T U,
+//          publish the next state operand
+//   output: O = Q+ S (before U is ready), then + P U, into the output tile
 template <typename E, int DK, int DVB, int C>
 __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH))
 __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, DVB, C>::WPE))) void state_pass_kernel(
@@ -596,7 +612,6 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   using M = typename S::M;
   using frag = typename S::frag;
   using St = typename E::storage;
-  constexpr int SPW = K::SPW;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
   const int chain = blockIdx.x, vb = blockIdx.y;
@@ -605,7 +620,6 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   const bool copier = wave >= K::NCW && wave < K::NCW + K::NCP;
   const bool storer = wave == K::NCW + K::NCP;
   const bool fetcher = wave == K::NCW + K::NCP + 1;
-  const bool computer = wave < K::NCW;
   const int cw = wave - K::NCW;  // copy-wave index
   const long rs = static_cast<long>(H) * DV;  // element stride between tokens
   const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
@@ -667,24 +681,36 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   };
 
   // --------------------------------------------------------- compute waves
+  // State wave of slab j (wave j) holds Sa[ti] = S[16 ti + 4 g + e][col] in
+  // accumulator registers; output wave of slab j is wave NSLAB + j.
   const int c16 = lane & 15, g = lane >> 4;
-  // Sa[j][ti] holds S[16 ti + 4 g + e][col(j)], col(j) = 16 (wave * SPW + j) + c16.
-  f32x4 Sa[SPW][S::NTK];
-  if (computer) {
+  const bool stater = wave < K::NSLAB;
+  const int slab = stater ? wave : wave - K::NSLAB;
+  const int col = vb * DVB + 16 * slab + c16;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  frag* xs = reinterpret_cast<frag*>(lds + K::OFF_XS) + slab * S::NKS * 64;  // + buffer * XS/FRAG*64
+  frag* xu = reinterpret_cast<frag*>(lds + K::OFF_XU) + slab * S::NCS * 64;
+  int* flag = reinterpret_cast<int*>(lds + K::OFF_FLAG) + slab;
+  constexpr int XSF = K::XS / S::FRAG * 64;  // frag elements per state buffer
+  f32x4 Sa[S::NTK];
+  frag sfr[S::NKS];  // bf16 (or fp32) operand copy of the state entering the chunk
+  if (stater) {
+    if (S0 != nullptr) {
+      const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
-      if (S0 != nullptr) {
-        const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+      for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-        for (int ti = 0; ti < S::NTK; ++ti)
+        for (int e = 0; e < 4; ++e) Sa[ti][e] = s0[(16 * ti + e) * DV];
+    } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Sa[j][ti][e] = s0[(16 * ti + e) * DV];
-      } else {
-#pragma unroll
-        for (int ti = 0; ti < S::NTK; ++ti) Sa[j][ti] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = z;
     }
+#pragma unroll
+    for (int s2 = 0; s2 < S::NKS; ++s2) {
+      sfr[s2] = M::from_acc(Sa[2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[2 * s2 + 1]);
+      xs[s2 * 64 + lane] = sfr[s2];
+    }
+    if (lane == 0) *flag = 0;
   } else if (copier && nchunk > 0) {
     stage_slot(0, 0);
     stage_v(0);
@@ -701,6 +727,10 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       __builtin_amdgcn_s_barrier();
     else
       __syncthreads();
+    const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
+    auto fr = [&](int off, int idx) -> frag {
+      return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
+    };
     if (storer) {
       if (n > 0) store_out(n - 1);  // its LDS reads complete before the stores issue
     } else if (fetcher) {
@@ -714,138 +744,117 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
         stage_v(n + 1);
       }
       if (K::NBUF == 2) __builtin_amdgcn_s_waitcnt(0);
-    } else {
+    } else if (stater) {
       // Each product first issues all of its LDS operand reads, then runs its
       // MFMAs with the independent accumulator chains interleaved (k-step
       // outermost), so the matrix pipe is not waiting on one chain.
-      const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
-      auto fr = [&](int off, int idx) -> frag {
-        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
-      };
       const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
-      St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
       const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-
       frag akp[S::NT][S::NKS];
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2) akp[tr][s2] = fr(S::OFF_KP, tr * S::NKS + s2);
-      float vr[SPW][S::NT][4];
+      float vr[S::NT][4];
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
+      for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vr[j][tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16);
-      frag sfr[SPW][S::NKS];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2)
-          sfr[j][s2] = M::from_acc(Sa[j][2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[j][2 * s2 + 1]);
+        for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16);
 
       // R = V - K+ S
-      f32x4 R[SPW][S::NT];
+      f32x4 R[S::NT];
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr) R[j][tr] = z;
+      for (int tr = 0; tr < S::NT; ++tr) R[tr] = z;
 #pragma unroll
       for (int s2 = 0; s2 < S::NKS; ++s2)
 #pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr)
-#pragma unroll
-          for (int j = 0; j < SPW; ++j) R[j][tr] = M::mma(akp[tr][s2], sfr[j][s2], R[j][tr]);
+        for (int tr = 0; tr < S::NT; ++tr) R[tr] = M::mma(akp[tr][s2], sfr[s2], R[tr]);
       frag atm[S::NTRI];
 #pragma unroll
       for (int i = 0; i < S::NTRI; ++i) atm[i] = fr(S::OFF_TM, i);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
+      for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr)
+        for (int e = 0; e < 4; ++e) R[tr][e] = (t0 + 16 * tr + 4 * g + e < T ? vr[tr][e] : 0.f) - R[tr][e];
+      frag rfr[S::NCS];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            R[j][tr][e] = (t0 + 16 * tr + 4 * g + e < T ? vr[j][tr][e] : 0.f) - R[j][tr][e];
-      frag rfr[SPW][S::NCS];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int s2 = 0; s2 < S::NCS; ++s2)
-          rfr[j][s2] = M::from_acc(R[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[j][2 * s2 + 1]);
+      for (int s2 = 0; s2 < S::NCS; ++s2)
+        rfr[s2] = M::from_acc(R[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : R[2 * s2 + 1]);
 
       // U = Tm R  (Tm lower triangular: row tile tr uses k-steps s2 <= tr / 2)
-      f32x4 U[SPW][S::NT];
+      f32x4 U[S::NT];
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr) U[j][tr] = z;
+      for (int tr = 0; tr < S::NT; ++tr) U[tr] = z;
 #pragma unroll
       for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
-        for (int tr = 2 * s2; tr < S::NT; ++tr)
-#pragma unroll
-          for (int j = 0; j < SPW; ++j) U[j][tr] = M::mma(atm[S::tri(tr) + s2], rfr[j][s2], U[j][tr]);
+        for (int tr = 2 * s2; tr < S::NT; ++tr) U[tr] = M::mma(atm[S::tri(tr) + s2], rfr[s2], U[tr]);
       frag akb[S::NTK][S::NCS];
 #pragma unroll
       for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
         for (int s2 = 0; s2 < S::NCS; ++s2) akb[ti][s2] = fr(S::OFF_KB, ti * S::NCS + s2);
-      frag ufr[SPW][S::NCS];
+      frag ufr[S::NCS];
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int s2 = 0; s2 < S::NCS; ++s2)
-          ufr[j][s2] = M::from_acc(U[j][2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[j][2 * s2 + 1]);
+      for (int s2 = 0; s2 < S::NCS; ++s2) {
+        ufr[s2] = M::from_acc(U[2 * s2], (S::CODD && s2 == S::NCS - 1) ? z : U[2 * s2 + 1]);
+        xu[s2 * 64 + lane] = ufr[s2];
+      }
+      // publish U to the output wave: its LDS writes complete before the count
+      if (lane == 0) __hip_atomic_store(flag, n + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
       // S <- Diag(gamma_C) S + Kbar^T U
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti) {
-        const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) Sa[j][ti] *= gc;
-      }
+      for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] *= *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
 #pragma unroll
       for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
-        for (int ti = 0; ti < S::NTK; ++ti)
+        for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = M::mma(akb[ti][s2], ufr[s2], Sa[ti]);
+      // the next chunk's state operand, for both waves of the slab
+      frag* xn = xs + ((n + 1) & 1) * XSF;
 #pragma unroll
-          for (int j = 0; j < SPW; ++j) Sa[j][ti] = M::mma(akb[ti][s2], ufr[j][s2], Sa[j][ti]);
-
-      // O = Q+ S_in + P U  (S_in is still held as the bf16 operand sfr)
-      frag aqp[S::NT][S::NKS], app[S::NTRI];
+      for (int s2 = 0; s2 < S::NKS; ++s2) {
+        sfr[s2] = M::from_acc(Sa[2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[2 * s2 + 1]);
+        xn[s2 * 64 + lane] = sfr[s2];
+      }
+    } else {
+      // Output wave: O = Q+ S_in + P U into the output tile.
+      St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
+      const frag* xc = xs + (n & 1) * XSF;
+      frag osf[S::NKS], aqp[S::NT][S::NKS];
+#pragma unroll
+      for (int s2 = 0; s2 < S::NKS; ++s2) osf[s2] = xc[s2 * 64 + lane];
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2) aqp[tr][s2] = fr(S::OFF_QP, tr * S::NKS + s2);
+      f32x4 O[S::NT];
 #pragma unroll
-      for (int i = 0; i < S::NTRI; ++i) app[i] = fr(S::OFF_PP, i);
-      f32x4 O[SPW][S::NT];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr) O[j][tr] = z;
+      for (int tr = 0; tr < S::NT; ++tr) O[tr] = z;
 #pragma unroll
       for (int s2 = 0; s2 < S::NKS; ++s2)
 #pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr)
+        for (int tr = 0; tr < S::NT; ++tr) O[tr] = M::mma(aqp[tr][s2], osf[s2], O[tr]);
+      frag app[S::NTRI];
 #pragma unroll
-          for (int j = 0; j < SPW; ++j) O[j][tr] = M::mma(aqp[tr][s2], sfr[j][s2], O[j][tr]);
+      for (int i = 0; i < S::NTRI; ++i) app[i] = fr(S::OFF_PP, i);
+      // U of this chunk: the state wave publishes it part-way through the
+      // chunk.  The wait is bounded; the state wave never waits on this wave.
+      for (int it = 0; it < (1 << 24); ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > n) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      frag ufr[S::NCS];
+#pragma unroll
+      for (int s2 = 0; s2 < S::NCS; ++s2) ufr[s2] = xu[s2 * 64 + lane];
 #pragma unroll
       for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
-        for (int tr = 2 * s2; tr < S::NT; ++tr)
+        for (int tr = 2 * s2; tr < S::NT; ++tr) O[tr] = M::mma(app[S::tri(tr) + s2], ufr[s2], O[tr]);
 #pragma unroll
-          for (int j = 0; j < SPW; ++j) O[j][tr] = M::mma(app[S::tri(tr) + s2], ufr[j][s2], O[j][tr]);
+      for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-      for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * (wave * SPW + j) + c16, O[j][tr][e]);
+        for (int e = 0; e < 4; ++e) store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16, O[tr][e]);
     }
     if (K::NBUF == 1) {
       if (storer || fetcher)
@@ -867,16 +876,12 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   }
   if (storer || fetcher) __builtin_amdgcn_s_waitcnt(0);
 
-  if (computer && ST != nullptr) {
+  if (stater && ST != nullptr) {
+    float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int col = vb * DVB + 16 * (wave * SPW + j) + c16;
-      float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+    for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[j][ti][e];
-    }
+      for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
   }
 }
 
