@@ -17,18 +17,21 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "KDA_F32", "KDA_BF16", "KdaError", "lib", "library_path", "exported_symbols",
+    "KDA_F32", "KDA_BF16", "GATES", "RULES", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
     "status_string", "version", "workspace_bytes",
 ]
 
 KDA_F32 = 0
 KDA_BF16 = 1
+# kda_gate / kda_rule of include/kda.h
+GATES = {"channel": 0, "head": 1, "none": 2}
+RULES = {"delta": 0, "linear": 1}
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
 # Every symbol include/kda.h declares.
-ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked",
-               "kda_fwd_chunked_workspace_bytes", "kda_decode_step")
+ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
+               "kda_fwd_chunked_workspace_bytes", "kda_decode_step", "kda_decode_step_ex")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -65,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_workspace_bytes.restype = sz
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.kda_decode_step.restype = i
+        L.kda_fwd_chunked_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                         i, i, vp, sz, vp]
+        L.kda_fwd_chunked_ex.restype = i
+        L.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+        L.kda_decode_step_ex.restype = i
         _lib = L
     return _lib
 
@@ -84,14 +92,17 @@ def status_string(status: int) -> str:
 
 # ---------------------------------------------------------------- raw calls
 def kda_fwd_chunked_raw(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
-                        workspace=None, workspace_bytes=0, stream=None) -> int:
+                        workspace=None, workspace_bytes=0, stream=None, gate=0, rule=0) -> int:
     """Direct C call with integer pointers (0/None for NULL); returns the status."""
-    return int(lib().kda_fwd_chunked(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v,
-                                     chunk, dtype, workspace, workspace_bytes, stream))
+    return int(lib().kda_fwd_chunked_ex(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v,
+                                        chunk, dtype, gate, rule, workspace, workspace_bytes,
+                                        stream))
 
 
-def kda_decode_step_raw(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream=None) -> int:
-    return int(lib().kda_decode_step(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream))
+def kda_decode_step_raw(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream=None,
+                        gate=0, rule=0) -> int:
+    return int(lib().kda_decode_step_ex(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, gate,
+                                        rule, stream))
 
 
 # ---------------------------------------------------------- torch front end
@@ -120,6 +131,14 @@ def _check(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _variant(gate: str, rule: str):
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}, got {gate!r}")
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)}, got {rule!r}")
+    return GATES[gate], RULES[rule]
+
+
 def _stream_handle(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -130,7 +149,8 @@ def workspace_bytes(B: int, T: int, H: int, d_k: int, d_v: int, chunk: int, dtyp
 
 
 def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S_T=None,
-                    return_state: bool = True, workspace=None):
+                    return_state: bool = True, workspace=None, gate: str = "channel",
+                    rule: str = "delta"):
     """Chunked KDA prefill on the GPU.
 
     q, k, alpha: [B,T,H,d_k]; v: [B,T,H,d_v]; beta: [B,T,H] (all bf16 or all
@@ -138,7 +158,10 @@ def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S
     S_T is None when return_state is False.  ``S_T`` may be S0 (in place).
     ``workspace`` is an optional uint8 device tensor of at least
     workspace_bytes(...) bytes; by default one is taken from torch's caching
-    allocator for the call.
+    allocator for the call.  ``gate``: "channel" (alpha [B,T,H,d_k], KDA),
+    "head" (alpha [B,T,H], Gated DeltaNet) or "none" (alpha ignored, may be
+    None).  ``rule``: "delta" (error-correcting write) or "linear" (no
+    correction).
     """
     torch = _torch()
     if q.dim() != 4:
@@ -147,8 +170,12 @@ def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S
     d_v = v.shape[-1]
     dt, dev = q.dtype, q.device
     _dtype_code(q)
+    g, r = _variant(gate, rule)
     _check(k, "k", (B, T, H, d_k), dt, dev)
-    _check(alpha, "alpha", (B, T, H, d_k), dt, dev)
+    if g == GATES["channel"]:
+        _check(alpha, "alpha", (B, T, H, d_k), dt, dev)
+    elif g == GATES["head"]:
+        _check(alpha, "alpha", (B, T, H), dt, dev)
     _check(v, "v", (B, T, H, d_v), dt, dev)
     _check(beta, "beta", (B, T, H), dt, dev)
     _check(q, "q", (B, T, H, d_k), dt, dev)
@@ -167,18 +194,22 @@ def kda_fwd_chunked(q, k, v, alpha, beta, S0=None, *, chunk: int = 64, o=None, S
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
         raise ValueError(f"workspace must hold {need} bytes on {dev}")
-    st = kda_fwd_chunked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+    ap = alpha.data_ptr() if (alpha is not None and g != GATES["none"]) else None
+    st = kda_fwd_chunked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), ap,
                              beta.data_ptr(), S0.data_ptr() if S0 is not None else None,
                              o.data_ptr(), S_T.data_ptr() if S_T is not None else None,
                              B, T, H, d_k, d_v, chunk, _dtype_code(q), workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), _stream_handle(dev))
+                             workspace.numel() * workspace.element_size(), _stream_handle(dev),
+                             g, r)
     if st != 0:
         raise KdaError(st, "kda_fwd_chunked")
     return o, S_T
 
 
-def kda_decode_step(q, k, v, alpha, beta, S, *, o=None):
-    """One T=1 decode step; S [B,H,d_k,d_v] fp32 is updated in place.  Returns o."""
+def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, gate: str = "channel",
+                    rule: str = "delta"):
+    """One T=1 decode step; S [B,H,d_k,d_v] fp32 is updated in place.  Returns o.
+    ``gate``/``rule`` as for kda_fwd_chunked (a "head" gate is alpha [B,H])."""
     torch = _torch()
     if q.dim() != 3:
         raise ValueError("q must be [B,H,d_k]")
@@ -186,8 +217,12 @@ def kda_decode_step(q, k, v, alpha, beta, S, *, o=None):
     d_v = v.shape[-1]
     dt, dev = q.dtype, q.device
     _dtype_code(q)
+    g, r = _variant(gate, rule)
     _check(k, "k", (B, H, d_k), dt, dev)
-    _check(alpha, "alpha", (B, H, d_k), dt, dev)
+    if g == GATES["channel"]:
+        _check(alpha, "alpha", (B, H, d_k), dt, dev)
+    elif g == GATES["head"]:
+        _check(alpha, "alpha", (B, H), dt, dev)
     _check(v, "v", (B, H, d_v), dt, dev)
     _check(beta, "beta", (B, H), dt, dev)
     _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
@@ -195,9 +230,10 @@ def kda_decode_step(q, k, v, alpha, beta, S, *, o=None):
         o = torch.empty((B, H, d_v), dtype=dt, device=dev)
     else:
         _check(o, "o", (B, H, d_v), dt, dev)
-    st = kda_decode_step_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+    ap = alpha.data_ptr() if (alpha is not None and g != GATES["none"]) else None
+    st = kda_decode_step_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), ap,
                              beta.data_ptr(), S.data_ptr(), o.data_ptr(), B, H, d_k, d_v,
-                             _dtype_code(q), _stream_handle(dev))
+                             _dtype_code(q), _stream_handle(dev), g, r)
     if st != 0:
         raise KdaError(st, "kda_decode_step")
     return o

@@ -12,6 +12,8 @@ constexpr int kVersion = 1;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool dtype_ok(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
+bool rule_ok(int r) { return r == KDA_RULE_DELTA || r == KDA_RULE_LINEAR; }
 
 int from_hip(hipError_t e) {
   if (e == hipSuccess) return KDA_OK;
@@ -45,21 +47,26 @@ size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v, in
   return static_cast<size_t>(B) * H * nchunk * slot;
 }
 
-int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
-                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
-                    int d_k, int d_v, int chunk, int dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, const float* S0, void* o, float* S_T, int B, int T,
+                       int H, int d_k, int d_v, int chunk, int dtype, int gate, int rule,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule))
+      return KDA_ERR_INVALID_ARG;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    const uintptr_t esz = dtype == KDA_BF16 ? 2 : 4;
     if (T > 0) {
-      if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
-      if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
-          !aligned16(o))
+      if (!q || !k || !v || !beta || !o || (gate != KDA_GATE_NONE && !alpha))
         return KDA_ERR_INVALID_ARG;
-      // beta is read one element at a time; natural alignment is enough
-      const uintptr_t esz = dtype == KDA_BF16 ? 2 : 4;
+      if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return KDA_ERR_INVALID_ARG;
+      // per-channel gates are read 16 bytes at a time; beta and per-head
+      // gates one element at a time, so natural alignment is enough
+      if (gate == KDA_GATE_CHANNEL && !aligned16(alpha)) return KDA_ERR_INVALID_ARG;
+      if (gate == KDA_GATE_HEAD && reinterpret_cast<uintptr_t>(alpha) % esz != 0)
+        return KDA_ERR_INVALID_ARG;
       if (reinterpret_cast<uintptr_t>(beta) % esz != 0) return KDA_ERR_INVALID_ARG;
     }
     if ((S0 && !aligned16(S0)) || (S_T && !aligned16(S_T))) return KDA_ERR_INVALID_ARG;
@@ -77,6 +84,7 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alp
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.chunk = chunk;
+    a.gate = gate; a.rule = rule;
     a.bf16 = dtype == KDA_BF16;
     a.workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
@@ -86,17 +94,29 @@ int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alp
   }
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
-                    const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
-                    int dtype, void* stream) {
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
+                    int d_k, int d_v, int chunk, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return kda_fwd_chunked_ex(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
+                            KDA_GATE_CHANNEL, KDA_RULE_DELTA, workspace, workspace_bytes, stream);
+}
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
+                       int dtype, int gate, int rule, void* stream) {
   try {
-    if (B < 1 || H < 1 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule))
+      return KDA_ERR_INVALID_ARG;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned16(S) ||
-        !aligned16(o))
+    if (!q || !k || !v || !beta || !S || !o || (gate != KDA_GATE_NONE && !alpha))
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(o))
       return KDA_ERR_INVALID_ARG;
     const uintptr_t esz = dtype == KDA_BF16 ? 2 : 4;
+    if (gate == KDA_GATE_CHANNEL && !aligned16(alpha)) return KDA_ERR_INVALID_ARG;
+    if (gate == KDA_GATE_HEAD && reinterpret_cast<uintptr_t>(alpha) % esz != 0)
+      return KDA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(beta) % esz != 0) return KDA_ERR_INVALID_ARG;
     if (static_cast<long long>(B) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
 
@@ -104,12 +124,20 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* alp
     a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
     a.S = S; a.o = o;
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.gate = gate; a.rule = rule;
     a.bf16 = dtype == KDA_BF16;
     a.stream = static_cast<hipStream_t>(stream);
     return from_hip(kda::launch_decode(a));
   } catch (...) {
     return KDA_ERR_HIP;
   }
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
+                    int dtype, void* stream) {
+  return kda_decode_step_ex(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, KDA_GATE_CHANNEL,
+                            KDA_RULE_DELTA, stream);
 }
 
 }  // extern "C"

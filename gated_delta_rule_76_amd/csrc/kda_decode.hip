@@ -6,8 +6,12 @@
 //   S' = Diag(alpha) S             decay every key channel (row of S)
 //   v_hat = S'^T k, z = S'^T q     two reductions over d_k, same pass over S
 //   u = beta (v - v_hat)           the delta rule's scaled prediction error
+//                                  (u = beta v without the correction)
 //   S <- S' + k u^T                written back in place
 //   o = z + (k^T q) u              = S_new^T q, no second pass over S
+//
+// The gate is one decay per key channel (KDA), one per head broadcast over the
+// channels (Gated DeltaNet), or none.
 //
 // The kernel is bound by HBM: it reads and writes each state once.  One
 // workgroup owns one head.  Thread t holds a float4 column group (4 adjacent
@@ -36,7 +40,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ v, const typename E::storage* __restrict__ alpha,
     const typename E::storage* __restrict__ beta, float* __restrict__ S,
-    typename E::storage* __restrict__ o) {
+    typename E::storage* __restrict__ o, int gate, int rule) {
   using Sh = DecodeShape<DK, DV>;
   const long head = blockIdx.x;  // b * H + h
   const int tid = threadIdx.x;
@@ -52,10 +56,12 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
 
   __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
   __shared__ float red[Sh::NW][2 * DV + 1];
+  // gate: one decay per channel, one per head (broadcast), or none
+  const float ah = gate == kGateHead ? load_scalar(alpha, head) : 1.f;
   for (int i = tid; i < DK; i += Sh::NTH) {
     sq[i] = load_scalar(q, head * DK + i);
     sk[i] = load_scalar(k, head * DK + i);
-    sa[i] = load_scalar(alpha, head * DK + i);
+    sa[i] = gate == kGateChannel ? load_scalar(alpha, head * DK + i) : ah;
   }
   for (int j = tid; j < DV; j += Sh::NTH) sv[j] = load_scalar(v, head * DV + j);
   const float bt = load_scalar(beta, head);
@@ -102,6 +108,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
       kq += r[2 * DV];
     }
   }
+  if (rule == kRuleLinear) y0 = y1 = y2 = y3 = 0.f;  // no correction: u = beta v
   const float u0 = bt * (sv[4 * cg + 0] - y0), u1 = bt * (sv[4 * cg + 1] - y1);
   const float u2 = bt * (sv[4 * cg + 2] - y2), u3 = bt * (sv[4 * cg + 3] - y3);
   if (rg == 0) {
@@ -127,7 +134,7 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
   hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(Sh::NTH), 0, a.stream,
                      static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                      static_cast<const St*>(a.v), static_cast<const St*>(a.alpha),
-                     static_cast<const St*>(a.beta), a.S, static_cast<St*>(a.o));
+                     static_cast<const St*>(a.beta), a.S, static_cast<St*>(a.o), a.gate, a.rule);
   return hipGetLastError();
 }
 

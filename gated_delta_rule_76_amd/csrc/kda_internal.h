@@ -5,11 +5,16 @@
 
 namespace kda {
 
+// Gate kinds and update rules, numbered as kda_gate / kda_rule in kda.h.
+constexpr int kGateChannel = 0, kGateHead = 1, kGateNone = 2;
+constexpr int kRuleDelta = 0, kRuleLinear = 1;
+
 struct DecodeArgs {
   const void *q, *k, *v, *alpha, *beta;
   float* S;
   void* o;
   int B, H, d_k, d_v;
+  int gate, rule;
   bool bf16;
   hipStream_t stream;
 };
@@ -20,6 +25,7 @@ struct PrefillArgs {
   void* o;
   float* S_T;
   int B, T, H, d_k, d_v, chunk;
+  int gate, rule;
   bool bf16;
   void* workspace;  // kda_fwd_chunked_workspace_bytes() bytes of device memory
   hipStream_t stream;

@@ -18,6 +18,11 @@
 // which unrolls the token recurrence exactly; the chunk's transition product
 // is Diag(gamma_C) - Kbar^T Tm K+, the page's P = D - K W^T.
 //
+// Variants: a per-head scalar gate (Gated DeltaNet) is the same algebra with
+// alpha broadcast over the channels; no gate sets alpha = 1.  Without the
+// correction (additive linear memory, section 2.1) there is no erase term:
+// A = 0, so Tm = Diag(beta) and R = V.
+//
 // Two kernels.
 //   chunk_prep_kernel: everything that does not depend on S, for every
 //     chunk of every (batch, head) at once (no sequential dependency).  Per
@@ -61,6 +66,11 @@ template <>
 struct Raw8<uint16_t> {
   uint4 r;
   __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void splat(const uint16_t* p) {  // one value in all 8 slots
+    const unsigned w = static_cast<unsigned>(*p) * 0x10001u;
+    r = uint4{w, w, w, w};
+  }
+  __device__ __forceinline__ void ones() { r = uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}; }
   __device__ __forceinline__ f32x8 unpack() const {
     f32x8 x;
     x[0] = __uint_as_float(r.x << 16); x[1] = __uint_as_float(r.x & 0xffff0000u);
@@ -77,6 +87,12 @@ struct Raw8<float> {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
   }
+  __device__ __forceinline__ void splat(const float* p) {
+    const float x = *p;
+    a = f32x4{x, x, x, x};
+    b = a;
+  }
+  __device__ __forceinline__ void ones() { a = b = f32x4{1.f, 1.f, 1.f, 1.f}; }
   __device__ __forceinline__ f32x8 unpack() const { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
 };
 
@@ -221,7 +237,7 @@ template <typename E, int DK, int C>
 __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ alpha, const typename E::storage* __restrict__ beta,
-    char* __restrict__ ws, int T, int H, int nchunk, int ntask) {
+    char* __restrict__ ws, int T, int H, int nchunk, int ntask, int gate, int rule) {
   using S = Shape<E, DK, C>;
   using P = PrepCfg<E, DK, C>;
   using M = typename S::M;
@@ -263,7 +279,12 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
         for (int rr = 0; rr < P::RPG; ++rr) {
           const long row = rowptr(task, rg * P::RPG + rr);
-          ra[rr].load(alpha + row * DK + ch0);
+          if (gate == kGateChannel)
+            ra[rr].load(alpha + row * DK + ch0);
+          else if (gate == kGateHead)
+            ra[rr].splat(alpha + row);  // one decay for every channel of the head
+          else
+            ra[rr].ones();
           rk[rr].load(k + row * DK + ch0);
           rq[rr].load(q + row * DK + ch0);
         }
@@ -452,7 +473,8 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * tr + 4 * g + e;
-            Mf[r * P::LDF + jc] = jc < r ? sm.beta[r] * acc[e] : 0.f;
+            // without the correction there is no erase term: A = 0, Tm = Diag(beta)
+            Mf[r * P::LDF + jc] = jc < r && rule == kRuleDelta ? sm.beta[r] * acc[e] : 0.f;
           }
         }
     }
@@ -606,7 +628,7 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH))
 __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, DVB, C>::WPE))) void state_pass_kernel(
     const char* __restrict__ ws, const typename E::storage* __restrict__ v,
     const float* __restrict__ S0, typename E::storage* __restrict__ o, float* __restrict__ ST,
-    int T, int H, int DV, int nchunk) {
+    int T, int H, int DV, int nchunk, int rule) {
   using S = Shape<E, DK, C>;
   using K = PassCfg<E, DK, DVB, C>;
   using M = typename S::M;
@@ -761,14 +783,16 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
         for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16);
 
-      // R = V - K+ S
+      // R = V - K+ S  (R = V without the correction)
       f32x4 R[S::NT];
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr) R[tr] = z;
+      if (rule == kRuleDelta) {
 #pragma unroll
-      for (int s2 = 0; s2 < S::NKS; ++s2)
+        for (int s2 = 0; s2 < S::NKS; ++s2)
 #pragma unroll
-        for (int tr = 0; tr < S::NT; ++tr) R[tr] = M::mma(akp[tr][s2], sfr[s2], R[tr]);
+          for (int tr = 0; tr < S::NT; ++tr) R[tr] = M::mma(akp[tr][s2], sfr[s2], R[tr]);
+      }
       frag atm[S::NTRI];
 #pragma unroll
       for (int i = 0; i < S::NTRI; ++i) atm[i] = fr(S::OFF_TM, i);
@@ -926,7 +950,7 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((chunk_prep_kernel<E, DK, C>), dim3(grid), dim3(NTH_PREP), 0, a.stream,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                        static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
-                       a.H, nchunk, static_cast<int>(ntask));
+                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -943,7 +967,7 @@ hipError_t launch_t(const PrefillArgs& a) {
   // one XCD (and its L2) whenever gridDim.x is a multiple of 8.
   hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, DV / DVB),
                      dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
-                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, DV, nchunk);
+                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, DV, nchunk, a.rule);
   return hipGetLastError();
 }
 

@@ -55,6 +55,28 @@ typedef enum {
     KDA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
 } kda_status;
 
+/*
+ * Gate and update-rule variants, for the *_ex entry points.
+ *
+ *   KDA_GATE_CHANNEL  alpha holds one decay per key channel, [.., d_k]: the
+ *                     KDA gate (section 4, vector gate alpha_t in [0,1]^{d_k}).
+ *   KDA_GATE_HEAD     alpha holds one scalar per (token, head), [..] like
+ *                     beta: the Gated DeltaNet forget gate that section 4
+ *                     starts from, S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1}
+ *                     + beta_t k_t v_t^T (a scalar commutes with the erase).
+ *   KDA_GATE_NONE     no decay (alpha = 1); the alpha pointer is not read and
+ *                     may be NULL.  With KDA_RULE_DELTA this is the plain
+ *                     delta rule of section 3.
+ *
+ *   KDA_RULE_DELTA    the error-correcting write: the erase term
+ *                     -beta_t k_t k_t^T acts on the decayed state (section 3).
+ *   KDA_RULE_LINEAR   no correction: S_t = Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *                     the plain additive linear memory of section 2.1 (with
+ *                     KDA_GATE_NONE and beta = 1 exactly S_t = S_{t-1} + k_t v_t^T).
+ */
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate;
+typedef enum { KDA_RULE_DELTA = 0, KDA_RULE_LINEAR = 1 } kda_rule;
+
 /* Library ABI version; bumped on any incompatible change. */
 KDA_API int kda_version(void);
 
@@ -102,6 +124,22 @@ KDA_API int kda_fwd_chunked(const void *q, const void *k, const void *v, const v
                     int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kda_fwd_chunked_ex -- kda_fwd_chunked with a gate and an update rule.
+ * Arguments as for kda_fwd_chunked, plus:
+ *   gate : kda_gate.  KDA_GATE_HEAD takes alpha as [B, T, H] (dtype);
+ *          KDA_GATE_NONE ignores alpha.
+ *   rule : kda_rule.
+ * kda_fwd_chunked(...) is kda_fwd_chunked_ex(..., KDA_GATE_CHANNEL,
+ * KDA_RULE_DELTA, ...).  The workspace size does not depend on gate or rule.
+ * A gate or rule outside the enums -> KDA_ERR_INVALID_ARG.
+ */
+KDA_API int kda_fwd_chunked_ex(const void *q, const void *k, const void *v, const void *alpha,
+                       const void *beta, const float *S0, void *o, float *S_T,
+                       int B, int T, int H, int d_k, int d_v, int chunk, int dtype,
+                       int gate, int rule, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* Bytes of workspace kda_fwd_chunked needs for these sizes:
  * B * H * ceil(T / chunk) * (bytes of one chunk's operand slot, about
  * 65 KiB at d_k = d_v = 128, chunk = 64, bf16).  0 for an unsupported or
@@ -128,6 +166,15 @@ KDA_API size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int
 KDA_API int kda_decode_step(const void *q, const void *k, const void *v, const void *alpha,
                     const void *beta, float *S, void *o, int B, int H, int d_k, int d_v,
                     int dtype, void *stream);
+
+/*
+ * kda_decode_step_ex -- kda_decode_step with a gate and an update rule (see
+ * kda_gate, kda_rule).  KDA_GATE_HEAD takes alpha as [B, H]; KDA_GATE_NONE
+ * ignores alpha.  KDA_RULE_LINEAR drops the prediction: u = beta v.
+ */
+KDA_API int kda_decode_step_ex(const void *q, const void *k, const void *v, const void *alpha,
+                       const void *beta, float *S, void *o, int B, int H, int d_k, int d_v,
+                       int dtype, int gate, int rule, void *stream);
 
 #ifdef __cplusplus
 }

@@ -75,16 +75,39 @@ def max_threads() -> int:
     return int(_load().kda_oracle_max_threads())
 
 
+def _gate_to_channels(alpha, gate: str, shape):
+    """The gate as one decay per key channel.  A per-head scalar gate (the
+    Gated DeltaNet form alpha_t (I - beta_t k_t k_t^T) S_{t-1}, page "Yanjiu
+    KimiK3 ...", section 4) is that scalar on every channel: a scalar
+    commutes with the erase, so it is the per-channel recurrence with all
+    channels equal.  No gate is alpha = 1."""
+    if gate == "channel":
+        return _f64(alpha)
+    if gate == "head":
+        return np.ascontiguousarray(np.broadcast_to(_f64(alpha)[..., None], shape))
+    if gate == "none":
+        return np.ones(shape, dtype=np.float64)
+    raise ValueError(f"unknown gate {gate!r}")
+
+
 def kda_forward(q, k, v, alpha, beta, S0=None, *, no_correction: bool = False,
+                gate: str = "channel", rule: str = "delta",
                 threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Token-by-token fp64 KDA forward.
 
-    q, k, alpha: [B,T,H,d_k]; v: [B,T,H,d_v]; beta: [B,T,H]; S0: [B,H,d_k,d_v]
-    or None (zero state).  Returns (o [B,T,H,d_v], S_T [B,H,d_k,d_v]), fp64.
+    q, k: [B,T,H,d_k]; alpha: [B,T,H,d_k] (gate "channel"), [B,T,H] (gate
+    "head") or ignored (gate "none"); v: [B,T,H,d_v]; beta: [B,T,H];
+    S0: [B,H,d_k,d_v] or None (zero state).  rule "linear" (or
+    no_correction=True) drops the prediction: the write is beta_t k_t v_t^T
+    (section 2.1's additive memory).  Returns (o [B,T,H,d_v], S_T), fp64.
     """
-    q, k, v, alpha, beta = (_f64(x) for x in (q, k, v, alpha, beta))
+    if rule not in ("delta", "linear"):
+        raise ValueError(f"unknown rule {rule!r}")
+    no_correction = no_correction or rule == "linear"
+    q, k, v, beta = (_f64(x) for x in (q, k, v, beta))
     if q.ndim != 4:
         raise ValueError("q must be [B,T,H,d_k]")
+    alpha = _gate_to_channels(alpha, gate, q.shape)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or alpha.shape != q.shape:
@@ -104,10 +127,13 @@ def kda_forward(q, k, v, alpha, beta, S0=None, *, no_correction: bool = False,
     return o, ST
 
 
-def kda_decode_step(q, k, v, alpha, beta, S, *, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-    """One T=1 step: q, k, alpha [B,H,d_k]; v [B,H,d_v]; beta [B,H]; S [B,H,d_k,d_v].
-    Returns (o [B,H,d_v], S_new), fp64.  Same recurrence as kda_forward."""
-    q, k, v, alpha = (_f64(x)[:, None] for x in (q, k, v, alpha))
+def kda_decode_step(q, k, v, alpha, beta, S, *, gate: str = "channel", rule: str = "delta",
+                    threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """One T=1 step: q, k [B,H,d_k]; alpha [B,H,d_k] / [B,H] / ignored by gate;
+    v [B,H,d_v]; beta [B,H]; S [B,H,d_k,d_v].  Returns (o [B,H,d_v], S_new),
+    fp64.  Same recurrence as kda_forward."""
+    q, k, v = (_f64(x)[:, None] for x in (q, k, v))
+    alpha = None if gate == "none" else _f64(alpha)[:, None]
     beta = _f64(beta)[:, None]
-    o, ST = kda_forward(q, k, v, alpha, beta, S, threads=threads)
+    o, ST = kda_forward(q, k, v, alpha, beta, S, gate=gate, rule=rule, threads=threads)
     return o[:, 0], ST

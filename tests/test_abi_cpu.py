@@ -116,3 +116,49 @@ def test_package_never_imports_the_oracle():
                         assert all(not a.name.startswith("oracle") for a in node.names), f
                     if isinstance(node, ast.ImportFrom):
                         assert not (node.module or "").startswith("oracle"), f
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate=3), 1), (dict(gate=-1), 1), (dict(rule=2), 1),
+    (dict(gate=0, alpha=None), 1),               # per-channel gate needs alpha
+    (dict(gate=1, alpha=None), 1),               # per-head gate needs alpha
+    (dict(gate=1, alpha=P + 1), 1),              # per-head gate: natural alignment
+    (dict(gate=0, alpha=P + 2), 1),              # per-channel gate: 16-byte alignment
+])
+def test_fwd_ex_validation(kw, code):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S0=None, o=P, S_T=P, B=1, T=64, H=1, d_k=64,
+             d_v=64, chunk=64, dtype=kda.KDA_BF16, ws=None, ws_bytes=0, gate=0, rule=0)
+    a.update(kw)
+    assert kda.kda_fwd_chunked_raw(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S0"], a["o"],
+                                   a["S_T"], a["B"], a["T"], a["H"], a["d_k"], a["d_v"], a["chunk"],
+                                   a["dtype"], a["ws"], a["ws_bytes"], None, a["gate"],
+                                   a["rule"]) == code
+
+
+def test_fwd_ex_gate_none_still_checks_the_workspace():
+    # alpha may be NULL without a gate; the call then fails on the missing
+    # workspace, before any launch
+    assert kda.kda_fwd_chunked_raw(P, P, P, None, P, None, P, P, 1, 64, 1, 64, 64, 64,
+                                   kda.KDA_BF16, None, 0, None, 2, 0) == 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate=5), 1), (dict(rule=9), 1), (dict(gate=0, alpha=None), 1),
+    (dict(gate=1, alpha=None), 1), (dict(gate=1, alpha=P + 1), 1),
+])
+def test_decode_ex_validation(kw, code):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, S=P, o=P, B=2, H=2, d_k=128, d_v=128,
+             dtype=kda.KDA_BF16, gate=0, rule=0)
+    a.update(kw)
+    assert kda.kda_decode_step_raw(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S"], a["o"],
+                                   a["B"], a["H"], a["d_k"], a["d_v"], a["dtype"], None,
+                                   a["gate"], a["rule"]) == code
+
+
+def test_torch_front_end_checks_gate_names():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.kda_fwd_chunked(q, q, q, q, torch.zeros(1, 4, 1), None, gate="vector")
+    with pytest.raises(ValueError):
+        kda.kda_fwd_chunked(q, q, q, q, torch.zeros(1, 4, 1), None, rule="gla")

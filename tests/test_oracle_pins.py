@@ -319,3 +319,73 @@ def test_no_correction_differs_from_delta():
     o1, _ = oracle.kda_forward(q, k, v, alpha, beta, S0)
     o2, _ = oracle.kda_forward(q, k, v, alpha, beta, S0, no_correction=True)
     assert _rel(o1, o2) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Gate and rule variants.
+#   Gated DeltaNet (section 4, the scalar forget gate KDA refines):
+#     S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+#     alpha_t one scalar per (token, head), coded here with dense matrices in
+#     exactly the page's order (gate outside the erase), independently of the
+#     oracle's per-channel loop.
+#   No gate with the delta rule is section 3's delta rule; no gate, no
+#   correction and beta = 1 is section 2.1's S_t = S_{t-1} + k_t v_t^T.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rule", ["delta", "linear"])
+def test_gdn_scalar_gate_page_form(rule):
+    rng = np.random.default_rng(41)
+    B, T, H, dk, dv = 1, 12, 2, 5, 3
+    q, k, v, _, beta, S0 = _rand_inputs(rng, B, T, H, dk, dv)
+    a = np.exp(-np.logaddexp(0, rng.standard_normal((B, T, H))) * 0.5)   # [B,T,H]
+    o, ST = oracle.kda_forward(q, k, v, a, beta, S0, gate="head", rule=rule)
+    for h in range(H):
+        S = S0[0, h].copy()
+        for t in range(T):
+            kt, vt, qt, bt, at = k[0, t, h], v[0, t, h], q[0, t, h], beta[0, t, h], a[0, t, h]
+            erase = np.eye(dk) - (bt * np.outer(kt, kt) if rule == "delta" else 0.0)
+            S = at * (erase @ S) + bt * np.outer(kt, vt)
+            assert _rel(o[0, t, h], S.T @ qt) < 1e-12
+        assert _rel(ST[0, h], S) < 1e-12
+
+
+def test_gate_none_is_the_plain_delta_rule():
+    rng = np.random.default_rng(42)
+    dk, dv, T = 6, 4, 30
+    q, k, v, _, beta, S0 = _rand_inputs(rng, 1, T, 1, dk, dv)
+    o, ST = oracle.kda_forward(q, k, v, None, beta, S0, gate="none")
+    S = S0[0, 0].copy()
+    for t in range(T):
+        kt, vt, qt, bt = k[0, t, 0], v[0, t, 0], q[0, t, 0], beta[0, t, 0]
+        S = S + bt * np.outer(kt, vt - S.T @ kt)        # error form, section 3
+        assert _rel(o[0, t, 0], S.T @ qt) < 1e-12
+    assert _rel(ST[0, 0], S) < 1e-12
+
+
+def test_gate_none_linear_beta_one_is_plain_linear_memory():
+    rng = np.random.default_rng(43)
+    T, dk, dv = 25, 7, 5
+    q, k, v, _, _, _ = _rand_inputs(rng, 1, T, 1, dk, dv)
+    o, ST = oracle.kda_forward(q, k, v, None, np.ones((1, T, 1)), None, gate="none", rule="linear")
+    Q, K, V = q[0, :, 0], k[0, :, 0], v[0, :, 0]
+    assert _rel(o[0, :, 0], np.tril(Q @ K.T) @ V) < 1e-13
+    assert _rel(ST[0, 0], K.T @ V) < 1e-13
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+@pytest.mark.parametrize("rule", ["delta", "linear"])
+def test_decode_step_variants_equal_one_token_prefill(gate, rule):
+    rng = np.random.default_rng(44)
+    B, H, dk, dv = 2, 3, 4, 5
+    q, k, v, alpha, beta, S0 = _rand_inputs(rng, B, 1, H, dk, dv)
+    a = {"channel": alpha[:, 0], "head": alpha[:, 0, :, 0], "none": None}[gate]
+    o1, S1 = oracle.kda_decode_step(q[:, 0], k[:, 0], v[:, 0], a, beta[:, 0], S0, gate=gate, rule=rule)
+    # the same step written out per head
+    for b in range(B):
+        for h in range(H):
+            at = {"channel": alpha[b, 0, h], "head": np.full(dk, alpha[b, 0, h, 0]), "none": np.ones(dk)}[gate]
+            Sd = at[:, None] * S0[b, h]
+            kt, vt, qt, bt = k[b, 0, h], v[b, 0, h], q[b, 0, h], beta[b, 0, h]
+            u = bt * (vt - (Sd.T @ kt if rule == "delta" else 0.0))
+            Sn = Sd + np.outer(kt, u)
+            assert _rel(S1[b, h], Sn) < 1e-13
+            assert _rel(o1[b, h], Sn.T @ qt) < 1e-13
