@@ -22,6 +22,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -34,10 +36,12 @@ DECODE = "decode_b256_h16"
 DECODE_POOL = 16
 
 
-def prefill_alg_bytes(B, T, H, dk, dv, elem=2) -> int:
+def prefill_alg_bytes(B, T, H, dk, dv, elem=2, gate_per_channel=True) -> int:
     """Algorithmic HBM bytes of one prefill call: read q, k, alpha, v, beta,
-    write o (elem bytes each), read S0 and write S_T (fp32)."""
-    per_tok_head = (3 * dk + dv) * elem + elem + dv * elem
+    write o (elem bytes each), read S0 and write S_T (fp32).  A per-head gate
+    is one element per token-head instead of d_k."""
+    ga = dk if gate_per_channel else 1
+    per_tok_head = (2 * dk + ga + dv) * elem + elem + dv * elem
     return B * T * H * per_tok_head + 2 * B * H * dk * dv * 4
 
 
@@ -114,13 +118,15 @@ def _time_launches(fn, steps: int, warmup: int):
     return t_start.elapsed_time(t_end) / 1e3, per
 
 
-def bench_prefill(name: str, steps: int, warmup: int):
+def bench_prefill(name: str, steps: int, warmup: int, gate: str = "channel"):
     import torch
     import gated_delta_rule_76_amd as kda
     from synth import WORKLOADS, workload_inputs
 
     w = WORKLOADS[name]
     x = workload_inputs(w)
+    if gate == "head":  # one decay per (token, head): the first channel of the drawn gate
+        x["alpha"] = np.ascontiguousarray(x["alpha"][..., 0])
     d = _upload(x, ("q", "k", "v", "alpha", "beta"), w.dtype)
     s0 = torch.from_numpy(x["S0"]).cuda()
     del x
@@ -132,7 +138,7 @@ def bench_prefill(name: str, steps: int, warmup: int):
 
     def fn():
         kda.kda_fwd_chunked(d["q"], d["k"], d["v"], d["alpha"], d["beta"], s0, chunk=w.chunk,
-                            o=o, S_T=st, workspace=ws)
+                            o=o, S_T=st, workspace=ws, gate=gate)
 
     total, per = _time_launches(fn, steps, warmup)
     ok = bool(torch.isfinite(o.float()).all().item() and torch.isfinite(st).all().item())
@@ -230,6 +236,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
 
@@ -293,6 +300,21 @@ def main():
                                "chunk": wl.chunk},
                     "hbm_frac": round(lby / (l_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # Gated DeltaNet variant (one decay per token and head) on the headline shape
+    gdn = None
+    if not args.no_gdn:
+        wg, gtot, gper, ok_g = bench_prefill(PREFILL, args.steps, args.warmup, gate="head")
+        g_ms = sum(gper) / len(gper)
+        gby = prefill_alg_bytes(wg.B, wg.T, wg.H, wg.d_k, wg.d_v, gate_per_channel=False)
+        gdn = {"value": round(wg.B * wg.T * args.steps / gtot, 1), "unit": "tokens/s",
+               "ms_per_call": round(g_ms, 4), "finite": ok_g, "gate": "head",
+               "config": {"workload": PREFILL, "batch": wg.B, "seq_len": wg.T, "heads": wg.H,
+                          "chunk": wg.chunk},
+               "roofline": {"bound": "hbm", "achieved": round(gby / (g_ms / 1e3) / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gby / (g_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "alg_bytes_per_launch": gby}}
+
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample_tokens)
 
     out = {
@@ -304,6 +326,7 @@ def main():
                    "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "state": "fp32",
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "long_context": long_ctx,
+        "gated_deltanet": gdn,
         "finite": bool(ok_p and ok_d),
     }
     print(json.dumps(out), flush=True)
