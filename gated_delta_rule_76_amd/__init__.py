@@ -19,6 +19,7 @@ from typing import Optional, Tuple
 __all__ = [
     "KDA_F32", "KDA_BF16", "GATES", "RULES", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
+    "kda_fwd_chunked_fused", "kda_decode_step_fused",
     "status_string", "version", "workspace_bytes",
 ]
 
@@ -31,7 +32,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
           3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
 # Every symbol include/kda.h declares.
 ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
-               "kda_fwd_chunked_workspace_bytes", "kda_decode_step", "kda_decode_step_ex")
+               "kda_fwd_chunked_fused", "kda_fwd_chunked_workspace_bytes", "kda_decode_step",
+               "kda_decode_step_ex", "kda_decode_step_fused")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -73,6 +75,12 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_ex.restype = i
         L.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
         L.kda_decode_step_ex.restype = i
+        f = ctypes.c_float
+        L.kda_fwd_chunked_fused.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i,
+                                            i, i, i, vp, sz, vp]
+        L.kda_fwd_chunked_fused.restype = i
+        L.kda_decode_step_fused.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, i, vp]
+        L.kda_decode_step_fused.restype = i
         _lib = L
     return _lib
 
@@ -103,6 +111,20 @@ def kda_decode_step_raw(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, strea
                         gate=0, rule=0) -> int:
     return int(lib().kda_decode_step_ex(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, gate,
                                         rule, stream))
+
+
+def kda_fwd_chunked_fused_raw(q_raw, k_raw, v, g_raw, b_raw, gate_scale, S0, o, S_T, B, T, H,
+                              d_k, d_v, chunk, dtype, gate, rule, workspace=None,
+                              workspace_bytes=0, stream=None) -> int:
+    return int(lib().kda_fwd_chunked_fused(q_raw, k_raw, v, g_raw, b_raw, float(gate_scale), S0, o,
+                                           S_T, B, T, H, d_k, d_v, chunk, dtype, gate, rule,
+                                           workspace, workspace_bytes, stream))
+
+
+def kda_decode_step_fused_raw(q_raw, k_raw, v, g_raw, b_raw, gate_scale, S, o, B, H, d_k, d_v,
+                              dtype, gate, rule, stream=None) -> int:
+    return int(lib().kda_decode_step_fused(q_raw, k_raw, v, g_raw, b_raw, float(gate_scale), S, o,
+                                           B, H, d_k, d_v, dtype, gate, rule, stream))
 
 
 # ---------------------------------------------------------- torch front end
@@ -236,4 +258,86 @@ def kda_decode_step(q, k, v, alpha, beta, S, *, o=None, gate: str = "channel",
                              _dtype_code(q), _stream_handle(dev), g, r)
     if st != 0:
         raise KdaError(st, "kda_decode_step")
+    return o
+
+
+def kda_fwd_chunked_fused(q_raw, k_raw, v, g_raw, b_raw, S0=None, *, gate_scale: float,
+                          chunk: int = 64, o=None, S_T=None, return_state: bool = True,
+                          workspace=None, gate: str = "channel", rule: str = "delta"):
+    """kda_fwd_chunked from raw projections: the kernels L2-normalise q_raw and
+    k_raw, map the gate as alpha = exp(-gate_scale * softplus(g_raw)) and beta =
+    sigmoid(b_raw).  Shapes as kda_fwd_chunked (g_raw [B,T,H] for gate "head")."""
+    torch = _torch()
+    if q_raw.dim() != 4:
+        raise ValueError("q_raw must be [B,T,H,d_k]")
+    B, T, H, d_k = q_raw.shape
+    d_v = v.shape[-1]
+    dt, dev = q_raw.dtype, q_raw.device
+    code = _dtype_code(q_raw)
+    g, r = _variant(gate, rule)
+    _check(k_raw, "k_raw", (B, T, H, d_k), dt, dev)
+    if g == GATES["channel"]:
+        _check(g_raw, "g_raw", (B, T, H, d_k), dt, dev)
+    elif g == GATES["head"]:
+        _check(g_raw, "g_raw", (B, T, H), dt, dev)
+    _check(v, "v", (B, T, H, d_v), dt, dev)
+    _check(b_raw, "b_raw", (B, T, H), dt, dev)
+    if S0 is not None:
+        _check(S0, "S0", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", (B, T, H, d_v), dt, dev)
+    if return_state and S_T is None:
+        S_T = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _check(S_T, "S_T", (B, H, d_k, d_v), torch.float32, dev)
+    need = workspace_bytes(B, T, H, d_k, d_v, chunk, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or workspace.device != dev:
+        raise ValueError(f"workspace must hold {need} bytes on {dev}")
+    gp = g_raw.data_ptr() if (g_raw is not None and g != GATES["none"]) else None
+    st = kda_fwd_chunked_fused_raw(q_raw.data_ptr(), k_raw.data_ptr(), v.data_ptr(), gp,
+                                   b_raw.data_ptr(), gate_scale,
+                                   S0.data_ptr() if S0 is not None else None, o.data_ptr(),
+                                   S_T.data_ptr() if S_T is not None else None, B, T, H, d_k, d_v,
+                                   chunk, code, g, r, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream_handle(dev))
+    if st != 0:
+        raise KdaError(st, "kda_fwd_chunked_fused")
+    return o, S_T
+
+
+def kda_decode_step_fused(q_raw, k_raw, v, g_raw, b_raw, S, *, gate_scale: float, o=None,
+                          gate: str = "channel", rule: str = "delta"):
+    """kda_decode_step from raw projections (maps as kda_fwd_chunked_fused).
+    S [B,H,d_k,d_v] fp32 is updated in place; returns o."""
+    torch = _torch()
+    if q_raw.dim() != 3:
+        raise ValueError("q_raw must be [B,H,d_k]")
+    B, H, d_k = q_raw.shape
+    d_v = v.shape[-1]
+    dt, dev = q_raw.dtype, q_raw.device
+    code = _dtype_code(q_raw)
+    g, r = _variant(gate, rule)
+    _check(k_raw, "k_raw", (B, H, d_k), dt, dev)
+    if g == GATES["channel"]:
+        _check(g_raw, "g_raw", (B, H, d_k), dt, dev)
+    elif g == GATES["head"]:
+        _check(g_raw, "g_raw", (B, H), dt, dev)
+    _check(v, "v", (B, H, d_v), dt, dev)
+    _check(b_raw, "b_raw", (B, H), dt, dev)
+    _check(S, "S", (B, H, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, H, d_v), dtype=dt, device=dev)
+    else:
+        _check(o, "o", (B, H, d_v), dt, dev)
+    gp = g_raw.data_ptr() if (g_raw is not None and g != GATES["none"]) else None
+    st = kda_decode_step_fused_raw(q_raw.data_ptr(), k_raw.data_ptr(), v.data_ptr(), gp,
+                                   b_raw.data_ptr(), gate_scale, S.data_ptr(), o.data_ptr(), B, H,
+                                   d_k, d_v, code, g, r, _stream_handle(dev))
+    if st != 0:
+        raise KdaError(st, "kda_decode_step_fused")
     return o

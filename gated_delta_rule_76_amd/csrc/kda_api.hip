@@ -14,6 +14,7 @@ bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool dtype_ok(int dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 bool gate_ok(int g) { return g == KDA_GATE_CHANNEL || g == KDA_GATE_HEAD || g == KDA_GATE_NONE; }
 bool rule_ok(int r) { return r == KDA_RULE_DELTA || r == KDA_RULE_LINEAR; }
+bool scale_ok(float c) { return c >= 0.f && c <= 3.0e38f; }  // finite, not negative (NaN fails)
 
 int from_hip(hipError_t e) {
   if (e == hipSuccess) return KDA_OK;
@@ -47,12 +48,17 @@ size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v, in
   return static_cast<size_t>(B) * H * nchunk * slot;
 }
 
-int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* alpha,
-                       const void* beta, const float* S0, void* o, float* S_T, int B, int T,
-                       int H, int d_k, int d_v, int chunk, int dtype, int gate, int rule,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+             const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
+             int chunk, int dtype, int gate, int rule, bool fused, float gate_scale,
+             void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule))
+    if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule) ||
+        !scale_ok(gate_scale))
       return KDA_ERR_INVALID_ARG;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
@@ -85,6 +91,7 @@ int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* 
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_v = d_v; a.chunk = chunk;
     a.gate = gate; a.rule = rule;
+    a.fused = fused; a.gate_scale = gate_scale;
     a.bf16 = dtype == KDA_BF16;
     a.workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
@@ -94,19 +101,12 @@ int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* 
   }
 }
 
-int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
-                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
-                    int d_k, int d_v, int chunk, int dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  return kda_fwd_chunked_ex(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
-                            KDA_GATE_CHANNEL, KDA_RULE_DELTA, workspace, workspace_bytes, stream);
-}
-
-int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
-                       const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
-                       int dtype, int gate, int rule, void* stream) {
+int decode_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
+                float* S, void* o, int B, int H, int d_k, int d_v, int dtype, int gate, int rule,
+                bool fused, float gate_scale, void* stream) {
   try {
-    if (B < 1 || H < 1 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule))
+    if (B < 1 || H < 1 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule) ||
+        !scale_ok(gate_scale))
       return KDA_ERR_INVALID_ARG;
     if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !beta || !S || !o || (gate != KDA_GATE_NONE && !alpha))
@@ -125,6 +125,7 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* 
     a.S = S; a.o = o;
     a.B = B; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.gate = gate; a.rule = rule;
+    a.fused = fused; a.gate_scale = gate_scale;
     a.bf16 = dtype == KDA_BF16;
     a.stream = static_cast<hipStream_t>(stream);
     return from_hip(kda::launch_decode(a));
@@ -133,11 +134,54 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* 
   }
 }
 
+}  // namespace
+
+extern "C" {
+
+int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, const float* S0, void* o, float* S_T, int B, int T,
+                       int H, int d_k, int d_v, int chunk, int dtype, int gate, int rule,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype, gate, rule,
+                  false, 0.f, workspace, workspace_bytes, stream);
+}
+
+int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,
+                    const void* beta, const float* S0, void* o, float* S_T, int B, int T, int H,
+                    int d_k, int d_v, int chunk, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
+                  KDA_GATE_CHANNEL, KDA_RULE_DELTA, false, 0.f, workspace, workspace_bytes, stream);
+}
+
+int kda_fwd_chunked_fused(const void* q_raw, const void* k_raw, const void* v, const void* g_raw,
+                          const void* b_raw, float gate_scale, const float* S0, void* o,
+                          float* S_T, int B, int T, int H, int d_k, int d_v, int chunk,
+                          int dtype, int gate, int rule, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return fwd_impl(q_raw, k_raw, v, g_raw, b_raw, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype,
+                  gate, rule, true, gate_scale, workspace, workspace_bytes, stream);
+}
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
+                       int dtype, int gate, int rule, void* stream) {
+  return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, gate, rule, false, 0.f,
+                     stream);
+}
+
+int kda_decode_step_fused(const void* q_raw, const void* k_raw, const void* v, const void* g_raw,
+                          const void* b_raw, float gate_scale, float* S, void* o, int B, int H,
+                          int d_k, int d_v, int dtype, int gate, int rule, void* stream) {
+  return decode_impl(q_raw, k_raw, v, g_raw, b_raw, S, o, B, H, d_k, d_v, dtype, gate, rule, true,
+                     gate_scale, stream);
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* alpha,
                     const void* beta, float* S, void* o, int B, int H, int d_k, int d_v,
                     int dtype, void* stream) {
-  return kda_decode_step_ex(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, KDA_GATE_CHANNEL,
-                            KDA_RULE_DELTA, stream);
+  return decode_impl(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, KDA_GATE_CHANNEL,
+                     KDA_RULE_DELTA, false, 0.f, stream);
 }
 
 }  // extern "C"

@@ -11,7 +11,9 @@
 //   o = z + (k^T q) u              = S_new^T q, no second pass over S
 //
 // The gate is one decay per key channel (KDA), one per head broadcast over the
-// channels (Gated DeltaNet), or none.
+// channels (Gated DeltaNet), or none.  With the fused prologue the inputs are
+// raw projections: q and k are L2-normalised, alpha = exp(-c softplus(g)),
+// beta = sigmoid(b), all in fp32 inside the kernel.
 //
 // The kernel is bound by HBM: it reads and writes each state once.  One
 // workgroup owns one head.  Thread t holds a float4 column group (4 adjacent
@@ -40,7 +42,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ v, const typename E::storage* __restrict__ alpha,
     const typename E::storage* __restrict__ beta, float* __restrict__ S,
-    typename E::storage* __restrict__ o, int gate, int rule) {
+    typename E::storage* __restrict__ o, int gate, int rule, int fused, float gscale) {
   using Sh = DecodeShape<DK, DV>;
   const long head = blockIdx.x;  // b * H + h
   const int tid = threadIdx.x;
@@ -56,16 +58,41 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
 
   __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
   __shared__ float red[Sh::NW][2 * DV + 1];
-  // gate: one decay per channel, one per head (broadcast), or none
-  const float ah = gate == kGateHead ? load_scalar(alpha, head) : 1.f;
+  // gate: one decay per channel, one per head (broadcast), or none; with the
+  // fused prologue the gate and beta arrive as raw projections
+  float ah = gate == kGateHead ? load_scalar(alpha, head) : 1.f;
+  if (fused && gate == kGateHead) ah = gate_map(ah, gscale);
   for (int i = tid; i < DK; i += Sh::NTH) {
     sq[i] = load_scalar(q, head * DK + i);
     sk[i] = load_scalar(k, head * DK + i);
-    sa[i] = gate == kGateChannel ? load_scalar(alpha, head * DK + i) : ah;
+    float a = ah;
+    if (gate == kGateChannel) {
+      a = load_scalar(alpha, head * DK + i);
+      if (fused) a = gate_map(a, gscale);
+    }
+    sa[i] = a;
   }
   for (int j = tid; j < DV; j += Sh::NTH) sv[j] = load_scalar(v, head * DV + j);
-  const float bt = load_scalar(beta, head);
+  float bt = load_scalar(beta, head);
+  if (fused) bt = sigmoid_f(bt);
   __syncthreads();
+  if (fused) {  // L2-normalise q and k: wave 0 reduces, everyone rescales
+    __shared__ float inv[2];
+    if (tid < 64) {
+      float ssq = 0.f, ssk = 0.f;
+      for (int i = tid; i < DK; i += 64) { ssq += sq[i] * sq[i]; ssk += sk[i] * sk[i]; }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) { ssq += __shfl_xor(ssq, off); ssk += __shfl_xor(ssk, off); }
+      if (tid == 0) {
+        inv[0] = ssq > 0.f ? rsqrtf(ssq) : 0.f;
+        inv[1] = ssk > 0.f ? rsqrtf(ssk) : 0.f;
+      }
+    }
+    __syncthreads();
+    const float iq = inv[0], ik = inv[1];
+    for (int i = tid; i < DK; i += Sh::NTH) { sq[i] *= iq; sk[i] *= ik; }
+    __syncthreads();
+  }
 
   float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
   float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
@@ -134,7 +161,8 @@ hipError_t launch_decode_t(const DecodeArgs& a) {
   hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(Sh::NTH), 0, a.stream,
                      static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                      static_cast<const St*>(a.v), static_cast<const St*>(a.alpha),
-                     static_cast<const St*>(a.beta), a.S, static_cast<St*>(a.o), a.gate, a.rule);
+                     static_cast<const St*>(a.beta), a.S, static_cast<St*>(a.o), a.gate, a.rule,
+                     a.fused ? 1 : 0, a.gate_scale);
   return hipGetLastError();
 }
 

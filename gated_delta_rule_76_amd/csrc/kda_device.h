@@ -36,4 +36,12 @@ __device__ __forceinline__ float load_scalar(const float* p, long i) { return p[
 __device__ __forceinline__ void store_scalar(uint16_t* p, long i, float x) { p[i] = f32_to_bf16_bits(x); }
 __device__ __forceinline__ void store_scalar(float* p, long i, float x) { p[i] = x; }
 
+// Input maps of the fused prologue, in fp32.
+//   softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^{-|x|})
+//   gate(x)     = exp(-c * softplus(x))       in (0, 1] for c > 0
+//   sigmoid(x)  = 1 / (1 + e^{-x})
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float gate_map(float x, float c) { return expf(-c * softplus_f(x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
 }  // namespace kda

@@ -15,6 +15,8 @@ struct DecodeArgs {
   void* o;
   int B, H, d_k, d_v;
   int gate, rule;
+  bool fused;        // inputs are raw projections: normalise q, k; map the gate and beta
+  float gate_scale;  // alpha = exp(-gate_scale * softplus(g)) when fused
   bool bf16;
   hipStream_t stream;
 };
@@ -26,6 +28,8 @@ struct PrefillArgs {
   float* S_T;
   int B, T, H, d_k, d_v, chunk;
   int gate, rule;
+  bool fused;        // inputs are raw projections: normalise q, k; map the gate and beta
+  float gate_scale;  // alpha = exp(-gate_scale * softplus(g)) when fused
   bool bf16;
   void* workspace;  // kda_fwd_chunked_workspace_bytes() bytes of device memory
   hipStream_t stream;

@@ -18,6 +18,11 @@
 // which unrolls the token recurrence exactly; the chunk's transition product
 // is Diag(gamma_C) - Kbar^T Tm K+, the page's P = D - K W^T.
 //
+// Fused prologue (optional): from raw projections the prep kernel forms
+// q / |q|, k / |k| per token and head, alpha = exp(-c softplus(g)) and
+// beta = sigmoid(b) in fp32 before anything else; the state pass only reads
+// the slot and v, so it is unaffected.
+//
 // Variants: a per-head scalar gate (Gated DeltaNet) is the same algebra with
 // alpha broadcast over the channels; no gate sets alpha = 1.  Without the
 // correction (additive linear memory, section 2.1) there is no erase term:
@@ -237,7 +242,8 @@ template <typename E, int DK, int C>
 __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ alpha, const typename E::storage* __restrict__ beta,
-    char* __restrict__ ws, int T, int H, int nchunk, int ntask, int gate, int rule) {
+    char* __restrict__ ws, int T, int H, int nchunk, int ntask, int gate, int rule, int fused,
+    float gscale) {
   using S = Shape<E, DK, C>;
   using P = PrepCfg<E, DK, C>;
   using M = typename S::M;
@@ -309,7 +315,11 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
       for (int rr = 0; rr < P::RPG; ++rr) {
         const bool ok = rg * P::RPG + rr < valid;
-        const f32x8 a = ra[rr].unpack();
+        f32x8 a = ra[rr].unpack();
+        if (fused && gate != kGateNone) {  // raw gate projection -> decay
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = gate_map(a[e], gscale);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) run[e] *= ok ? a[e] : 1.f;
         lg[rr] = run;
@@ -317,7 +327,10 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) scan[rg * DK + ch0 + e] = run[e];
     }
-    if (tid < C) sm.beta[tid] = tid < valid ? load_scalar(&rb, 0) : 0.f;
+    if (tid < C) {
+      const float bx = load_scalar(&rb, 0);
+      sm.beta[tid] = tid < valid ? (fused ? sigmoid_f(bx) : bx) : 0.f;
+    }
     __syncthreads();
     if (tid < DK) {  // exclusive products of the row-group totals, per channel
       float tot[P::NRG];
@@ -345,7 +358,22 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       for (int rr = 0; rr < P::RPG; ++rr) {
         const int r = rg * P::RPG + rr;
         const bool ok = r < valid;  // rows past the sequence: k = q = 0
-        const f32x8 kk = rk[rr].unpack(), qq = rq[rr].unpack();
+        f32x8 kk = rk[rr].unpack(), qq = rq[rr].unpack();
+        if (fused) {
+          // L2-normalise the token's key and query: the NCG threads of a row
+          // hold its channels in 8-wide groups (adjacent lanes).
+          float sk = 0.f, sq = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { sk += kk[e] * kk[e]; sq += qq[e] * qq[e]; }
+#pragma unroll
+          for (int off = 1; off < P::NCG; off <<= 1) {
+            sk += __shfl_xor(sk, off);
+            sq += __shfl_xor(sq, off);
+          }
+          const float ik = sk > 0.f ? rsqrtf(sk) : 0.f, iq = sq > 0.f ? rsqrtf(sq) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { kk[e] *= ik; qq[e] *= iq; }
+        }
         f32x8 kp, qp, km, kb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -950,7 +978,8 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((chunk_prep_kernel<E, DK, C>), dim3(grid), dim3(NTH_PREP), 0, a.stream,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                        static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
-                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule);
+                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
+                       a.gate_scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -140,6 +140,29 @@ KDA_API int kda_fwd_chunked_ex(const void *q, const void *k, const void *v, cons
                        int gate, int rule, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/*
+ * kda_fwd_chunked_fused -- kda_fwd_chunked_ex from raw projections, with the
+ * input maps applied inside the kernels in fp32 (the step before the
+ * recurrence: unit keys for the projection reading of section 3, a gate in
+ * [0, 1] per section 4):
+ *   q_raw, k_raw : [B, T, H, d_k] dtype; the library uses q = q_raw / |q_raw|
+ *                  and k = k_raw / |k_raw| per (token, head) (a zero vector
+ *                  stays zero)
+ *   g_raw        : gate projection, [B, T, H, d_k] (KDA_GATE_CHANNEL) or
+ *                  [B, T, H] (KDA_GATE_HEAD), dtype; alpha = exp(-gate_scale *
+ *                  softplus(g_raw)), softplus(x) = log(1 + e^x).  Ignored
+ *                  (may be NULL) with KDA_GATE_NONE.
+ *   b_raw        : [B, T, H] dtype; beta = sigmoid(b_raw) = 1 / (1 + e^-b_raw)
+ *   gate_scale   : c >= 0, finite; otherwise KDA_ERR_INVALID_ARG
+ * v is used as given.  All other arguments, the workspace and the semantics
+ * are those of kda_fwd_chunked_ex.
+ */
+KDA_API int kda_fwd_chunked_fused(const void *q_raw, const void *k_raw, const void *v,
+                          const void *g_raw, const void *b_raw, float gate_scale,
+                          const float *S0, void *o, float *S_T, int B, int T, int H, int d_k,
+                          int d_v, int chunk, int dtype, int gate, int rule, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace kda_fwd_chunked needs for these sizes:
  * B * H * ceil(T / chunk) * (bytes of one chunk's operand slot, about
  * 65 KiB at d_k = d_v = 128, chunk = 64, bf16).  0 for an unsupported or
@@ -175,6 +198,17 @@ KDA_API int kda_decode_step(const void *q, const void *k, const void *v, const v
 KDA_API int kda_decode_step_ex(const void *q, const void *k, const void *v, const void *alpha,
                        const void *beta, float *S, void *o, int B, int H, int d_k, int d_v,
                        int dtype, int gate, int rule, void *stream);
+
+/*
+ * kda_decode_step_fused -- kda_decode_step_ex from raw projections, with the
+ * same input maps as kda_fwd_chunked_fused (q, k L2-normalised; alpha =
+ * exp(-gate_scale * softplus(g_raw)); beta = sigmoid(b_raw)).  g_raw is
+ * [B, H, d_k] or [B, H] by gate; b_raw is [B, H].
+ */
+KDA_API int kda_decode_step_fused(const void *q_raw, const void *k_raw, const void *v,
+                          const void *g_raw, const void *b_raw, float gate_scale, float *S,
+                          void *o, int B, int H, int d_k, int d_v, int dtype, int gate, int rule,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -137,3 +137,31 @@ def kda_decode_step(q, k, v, alpha, beta, S, *, gate: str = "channel", rule: str
     beta = _f64(beta)[:, None]
     o, ST = kda_forward(q, k, v, alpha, beta, S, gate=gate, rule=rule, threads=threads)
     return o[:, 0], ST
+
+
+def input_prologue(q_raw, k_raw, g_raw, b_raw, gate_scale: float, gate: str = "channel"):
+    """The input maps in front of the recurrence, in fp64 (the fused kernels
+    apply them in fp32): unit query and key per (token, head) (the projection
+    reading of the delta rule, page "Yanjiu KimiK3 ...", section 3, needs unit
+    keys), a gate in [0, 1] (section 4) as alpha = exp(-c softplus(g)), and
+    beta = sigmoid(b).  A zero vector stays zero.  Returns (q, k, alpha, beta);
+    alpha keeps g_raw's shape (None for gate "none")."""
+    def unit(x):
+        x = _f64(x)
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+    q, k = unit(q_raw), unit(k_raw)
+    alpha = None
+    if gate != "none":
+        g = _f64(g_raw)
+        softplus = np.maximum(g, 0.0) + np.log1p(np.exp(-np.abs(g)))
+        alpha = np.exp(-float(gate_scale) * softplus)
+    beta = 1.0 / (1.0 + np.exp(-_f64(b_raw)))
+    return q, k, alpha, beta
+
+
+def kda_forward_fused(q_raw, k_raw, v, g_raw, b_raw, S0=None, *, gate_scale: float,
+                      gate: str = "channel", rule: str = "delta", threads: int = 0):
+    """kda_forward on the prologue's outputs (fp64 end to end)."""
+    q, k, alpha, beta = input_prologue(q_raw, k_raw, g_raw, b_raw, gate_scale, gate)
+    return kda_forward(q, k, v, alpha, beta, S0, gate=gate, rule=rule, threads=threads)

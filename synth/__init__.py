@@ -233,3 +233,23 @@ def orthonormal_key_set(d: int, kind: str = "hadamard") -> np.ndarray:
             raise ValueError("1/sqrt(d) is not exact in bf16 for this d")
         return out
     raise ValueError(kind)
+
+
+def raw_prefill_inputs(B: int, T: int, H: int, d_k: int, d_v: int, *, dtype: str = "bf16",
+                       s0_std: float = 0.01, seed: int = 0) -> dict:
+    """Raw projections for the fused prologue: q_raw, k_raw [B,T,H,d_k],
+    v [B,T,H,d_v], g_raw [B,T,H,d_k] (a per-head gate takes [..., 0]),
+    b_raw [B,T,H], all N(0, 1) draws (bf16-exact when dtype == "bf16"), and
+    S0 = s0_std * N(0, 1) fp32.  No maps are applied here."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7777])))
+    out = {
+        "q_raw": rng.standard_normal((B, T, H, d_k), dtype=np.float32),
+        "k_raw": rng.standard_normal((B, T, H, d_k), dtype=np.float32),
+        "v": rng.standard_normal((B, T, H, d_v), dtype=np.float32),
+        "g_raw": rng.standard_normal((B, T, H, d_k), dtype=np.float32),
+        "b_raw": rng.standard_normal((B, T, H), dtype=np.float32),
+    }
+    if dtype == "bf16":
+        out = {n: round_to_bf16(a) for n, a in out.items()}
+    out["S0"] = (s0_std * rng.standard_normal((B, H, d_k, d_v))).astype(np.float32) if s0_std > 0 else None
+    return out

@@ -162,3 +162,21 @@ def test_torch_front_end_checks_gate_names():
         kda.kda_fwd_chunked(q, q, q, q, torch.zeros(1, 4, 1), None, gate="vector")
     with pytest.raises(ValueError):
         kda.kda_fwd_chunked(q, q, q, q, torch.zeros(1, 4, 1), None, rule="gla")
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=-0.1), 1), (dict(c=float("nan")), 1), (dict(c=float("inf")), 1),
+    (dict(gate=4), 1), (dict(g=None, gate=0), 1),
+])
+def test_fwd_fused_validation(kw, code):
+    a = dict(c=0.1, gate=0, rule=0, g=P)
+    a.update(kw)
+    assert kda.kda_fwd_chunked_fused_raw(P, P, P, a["g"], P, a["c"], None, P, P, 1, 64, 1, 64, 64,
+                                         64, kda.KDA_BF16, a["gate"], a["rule"]) == code
+
+
+def test_decode_fused_validation():
+    assert kda.kda_decode_step_fused_raw(P, P, P, P, P, -1.0, P, P, 2, 2, 128, 128, kda.KDA_BF16,
+                                         0, 0) == 1
+    assert kda.kda_decode_step_fused_raw(P, P, P, None, P, 0.1, P, P, 2, 2, 128, 128, kda.KDA_BF16,
+                                         1, 0) == 1

@@ -113,3 +113,68 @@ def test_head_gate_equals_broadcast_channel_gate_bitwise():
     o1, s1 = _prefill(xa, "bf16", 64, "head", "delta")
     o2, s2 = _prefill(xa, "bf16", 64, "channel", "delta")
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+# ---------------------------------------------------------- fused prologue
+from synth import raw_prefill_inputs  # noqa: E402
+
+
+def _graw(x, gate):
+    return {"channel": x["g_raw"], "head": np.ascontiguousarray(x["g_raw"][..., 0]), "none": None}[gate]
+
+
+FUSED = [
+    # dtype, d_k, d_v, C, B, T, H, gate, rule
+    ("f32", 32, 32, 16, 1, 100, 2, "channel", "delta"),
+    ("f32", 64, 64, 32, 1, 70, 2, "head", "linear"),
+    ("bf16", 128, 128, 64, 1, 200, 2, "channel", "delta"),
+    ("bf16", 128, 128, 64, 2, 130, 2, "head", "delta"),
+    ("bf16", 64, 128, 32, 1, 99, 3, "none", "delta"),
+    ("bf16", 16, 32, 16, 1, 50, 2, "channel", "linear"),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C,B,T,H,gate,rule", FUSED)
+def test_prefill_fused_prologue(dtype, dk, dv, C, B, T, H, gate, rule):
+    import torch
+    import gated_delta_rule_76_amd as kda
+    name = f"prefill fused gate={gate} rule={rule} {dtype} dk{dk} dv{dv} C{C} B{B} T{T} H{H}"
+    log(f"[{name}]")
+    x = raw_prefill_inputs(B, T, H, dk, dv, dtype=dtype, s0_std=0.05, seed=dk + T)
+    c = 0.1
+    q, k, v, b = (to_dev(x[n], dtype) for n in ("q_raw", "k_raw", "v", "b_raw"))
+    g = _graw(x, gate)
+    gd = None if g is None else to_dev(g, dtype)
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o, st = kda.kda_fwd_chunked_fused(q, k, v, gd, b, s0, gate_scale=c, chunk=C, gate=gate, rule=rule)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_forward_fused(x["q_raw"], x["k_raw"], x["v"], g, x["b_raw"], x["S0"],
+                                            gate_scale=c, gate=gate, rule=rule)
+    eo, es = rel_err(to_np(o), o_ref), rel_err(to_np(st), s_ref)
+    log(f"  rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,gate", [("f32", "channel"), ("bf16", "channel"), ("bf16", "head"),
+                                        ("bf16", "none")])
+def test_decode_fused_prologue(dtype, gate):
+    import torch
+    import gated_delta_rule_76_amd as kda
+    B, H, dk, dv, steps, c = 4, 3, 128, 128, 8, 0.05
+    log(f"[decode fused gate={gate} {dtype} B{B} H{H} x{steps}]")
+    x = raw_prefill_inputs(B, steps, H, dk, dv, dtype=dtype, s0_std=0.05, seed=11)
+    S = torch.from_numpy(x["S0"]).cuda()
+    Sref = x["S0"].astype(np.float64)
+    for i in range(steps):
+        sl = {n: np.ascontiguousarray(x[n][:, i]) for n in ("q_raw", "k_raw", "v", "g_raw", "b_raw")}
+        g = {"channel": sl["g_raw"], "head": np.ascontiguousarray(sl["g_raw"][..., 0]), "none": None}[gate]
+        d = {n: to_dev(sl[n], dtype) for n in ("q_raw", "k_raw", "v", "b_raw")}
+        o = kda.kda_decode_step_fused(d["q_raw"], d["k_raw"], d["v"], None if g is None else to_dev(g, dtype),
+                                      d["b_raw"], S, gate_scale=c, gate=gate)
+        q, k, a, b = oracle.input_prologue(sl["q_raw"], sl["k_raw"], g, sl["b_raw"], c, gate)
+        o_ref, Sref = oracle.kda_decode_step(q, k, sl["v"], a, b, Sref, gate=gate)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(o), o_ref) <= TOL[dtype]
+    es = rel_err(S.cpu().numpy(), Sref)
+    log(f"  rel_err S after {steps} steps {es:.2e}")
+    assert es <= TOL[dtype]

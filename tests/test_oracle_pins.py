@@ -389,3 +389,47 @@ def test_decode_step_variants_equal_one_token_prefill(gate, rule):
             Sn = Sd + np.outer(kt, u)
             assert _rel(S1[b, h], Sn) < 1e-13
             assert _rel(o1[b, h], Sn.T @ qt) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# Input prologue (the maps in front of the recurrence): unit q and k per
+# (token, head), alpha = exp(-c softplus(g)) in (0, 1], beta = sigmoid(b).
+# Pinned by closed forms and by independent library routines.
+# --------------------------------------------------------------------------
+def test_prologue_unit_vectors_and_zero():
+    rng = np.random.default_rng(50)
+    q_raw = rng.standard_normal((2, 3, 4, 16)) * 7.0
+    k_raw = rng.standard_normal((2, 3, 4, 16))
+    k_raw[1, 2, 3] = 0.0
+    q, k, _, _ = oracle.input_prologue(q_raw, k_raw, None, np.zeros((2, 3, 4)), 0.1, gate="none")
+    assert np.allclose(np.linalg.norm(q, axis=-1), 1.0, rtol=0, atol=1e-14)
+    # same direction: q = q_raw / |q_raw| component-wise
+    cos = np.sum(q * q_raw, axis=-1) / np.linalg.norm(q_raw, axis=-1)
+    assert np.allclose(cos, 1.0, rtol=0, atol=1e-14)
+    assert np.all(k[1, 2, 3] == 0.0)
+    nz = np.linalg.norm(k, axis=-1)
+    nz[1, 2, 3] = 1.0
+    assert np.allclose(nz, 1.0, rtol=0, atol=1e-14)
+
+
+def test_prologue_gate_and_beta_closed_forms():
+    c = 0.37
+    g = np.array([0.0, 30.0, -30.0, 1.5, -2.25])
+    _, _, alpha, beta = oracle.input_prologue(np.ones((5, 2)), np.ones((5, 2)), g, g, c, gate="head")
+    assert abs(alpha[0] - 2.0 ** (-c)) < 1e-15                    # softplus(0) = ln 2
+    assert abs(np.log(alpha[1]) + c * 30.0) < 1e-12                # softplus(x) -> x
+    assert abs(alpha[2] - 1.0) < 1e-12                             # softplus(x) -> 0
+    assert abs(beta[0] - 0.5) < 1e-16
+    # independent routines: log(1 + e^x) as logaddexp(0, x); the logistic as tanh
+    assert np.allclose(alpha, np.exp(-c * np.logaddexp(0.0, g)), rtol=1e-14, atol=0)
+    assert np.allclose(beta, 0.5 * (1.0 + np.tanh(0.5 * g)), rtol=1e-14, atol=1e-16)
+    assert np.all((alpha > 0) & (alpha <= 1))
+
+
+def test_prologue_feeds_the_recurrence():
+    x = __import__("synth").raw_prefill_inputs(1, 9, 2, 8, 4, dtype="f32", s0_std=0.1, seed=3)
+    o1, s1 = oracle.kda_forward_fused(x["q_raw"], x["k_raw"], x["v"], x["g_raw"], x["b_raw"], x["S0"],
+                                      gate_scale=0.2)
+    q, k, a, b = oracle.input_prologue(x["q_raw"], x["k_raw"], x["g_raw"], x["b_raw"], 0.2)
+    o2, s2 = oracle.kda_forward(q, k, x["v"], a, b, x["S0"])
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
