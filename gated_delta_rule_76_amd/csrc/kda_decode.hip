@@ -37,13 +37,21 @@ struct DecodeShape {
   static_assert(NTH % 64 == 0 && RPT >= 1 && CG <= 64, "decode shape");
 };
 
-template <typename E, int DK, int DV>
+// PLAIN: the KDA step itself (per-channel gate, delta rule, inputs as given),
+// compiled without the variant branches; the general kernel reads gate, rule
+// and fused at run time.
+template <typename E, int DK, int DV, bool PLAIN>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ v, const typename E::storage* __restrict__ alpha,
     const typename E::storage* __restrict__ beta, float* __restrict__ S,
     typename E::storage* __restrict__ o, int gate, int rule, int fused, float gscale) {
   using Sh = DecodeShape<DK, DV>;
+  if constexpr (PLAIN) {
+    gate = kGateChannel;
+    rule = kRuleDelta;
+    fused = 0;
+  }
   const long head = blockIdx.x;  // b * H + h
   const int tid = threadIdx.x;
   const int cg = tid % Sh::CG;
@@ -158,7 +166,9 @@ template <typename E, int DK, int DV>
 hipError_t launch_decode_t(const DecodeArgs& a) {
   using Sh = DecodeShape<DK, DV>;
   using St = typename E::storage;
-  hipLaunchKernelGGL((decode_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(Sh::NTH), 0, a.stream,
+  const bool plain = a.gate == kGateChannel && a.rule == kRuleDelta && !a.fused;
+  auto kern = plain ? decode_kernel<E, DK, DV, true> : decode_kernel<E, DK, DV, false>;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(Sh::NTH), 0, a.stream,
                      static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                      static_cast<const St*>(a.v), static_cast<const St*>(a.alpha),
                      static_cast<const St*>(a.beta), a.S, static_cast<St*>(a.o), a.gate, a.rule,
