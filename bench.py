@@ -180,6 +180,33 @@ def bench_decode(steps: int, warmup: int):
     return w, total, per, ok
 
 
+ATTNRES = dict(L=64, N=4096, d_k=128, d=4096)  # earlier layers, tokens, key and model width
+
+
+def attnres_alg_bytes(L, N, dk, d, elem=2) -> int:
+    """Read h (L*N*d), k (L*N*d_k), q (N*d_k); write out (N*d)."""
+    return (L * N * d + L * N * dk + N * dk + N * d) * elem
+
+
+def bench_attnres(steps: int, warmup: int):
+    """AttnRes depth aggregation on seeded synthetic bf16 tensors generated on
+    the GPU (torch's generator, seed 0): q, k scaled so q.k has unit variance."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    c = ATTNRES
+    g = torch.Generator(device="cuda").manual_seed(0)
+    s = c["d_k"] ** -0.25
+    q = (s * torch.randn(c["N"], c["d_k"], generator=g, device="cuda")).to(torch.bfloat16)
+    k = (s * torch.randn(c["L"], c["N"], c["d_k"], generator=g, device="cuda")).to(torch.bfloat16)
+    h = torch.randn(c["L"], c["N"], c["d"], generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty(c["N"], c["d"], dtype=torch.bfloat16, device="cuda")
+    total, per = _time_launches(lambda: kda.attnres_forward(q, k, h, out=out), steps, warmup)
+    ok = bool(torch.isfinite(out.float()).all().item())
+    del q, k, h, out
+    torch.cuda.empty_cache()
+    return total, per, ok
+
+
 def cpu_baseline(sample_tokens: int):
     """Time the fp64 oracle on the first `sample_tokens` positions of every
     (batch, head) chain of the prefill workload on all host cores, and on one
@@ -209,7 +236,8 @@ def cpu_baseline(sample_tokens: int):
 
 def profile_pass():
     """Fixed short run for rocprofv3 counter passes: a plain 1 GiB copy (the
-    calibration kernel), 3 prefill launches, 3 decode launches."""
+    calibration kernel), 3 prefill launches, 3 decode launches, 3 AttnRes
+    launches."""
     import torch
     n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
     src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -224,6 +252,8 @@ def profile_pass():
     print("prefill: 3 launches", flush=True)
     bench_decode(3, 0)
     print("decode: 3 launches", flush=True)
+    bench_attnres(3, 0)
+    print("attnres: 3 launches", flush=True)
 
 
 def main():
@@ -237,6 +267,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
+    ap.add_argument("--no-attnres", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
 
@@ -315,6 +346,22 @@ def main():
                             "frac": round(gby / (g_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                             "alg_bytes_per_launch": gby}}
 
+    attnres = None
+    if not args.no_attnres:
+        atot, aper, ok_a = bench_attnres(args.steps, args.warmup)
+        a_ms = sum(aper) / len(aper)
+        c = ATTNRES
+        aby = attnres_alg_bytes(c["L"], c["N"], c["d_k"], c["d"])
+        attnres = {"value": round(c["N"] * args.steps / atot, 1), "unit": "tokens/s",
+                   "ms_per_call": round(a_ms, 4), "finite": ok_a,
+                   "config": {"workload": "attnres_l64_n4096_d4096", "layers": c["L"],
+                              "tokens": c["N"], "d_k": c["d_k"], "d": c["d"], "dtype": "bf16"},
+                   "roofline": {"bound": "hbm", "achieved": round(aby / (a_ms / 1e3) / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(aby / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "alg_bytes_per_launch": aby,
+                                "launch": "one attnres_forward call: attnres_kernel"}}
+
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample_tokens)
 
     out = {
@@ -326,7 +373,7 @@ def main():
                    "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "state": "fp32",
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "long_context": long_ctx,
-        "gated_deltanet": gdn,
+        "gated_deltanet": gdn, "attnres": attnres,
         "finite": bool(ok_p and ok_d),
     }
     print(json.dumps(out), flush=True)

@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 __all__ = [
     "KDA_F32", "KDA_BF16", "GATES", "RULES", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
-    "kda_fwd_chunked_fused", "kda_decode_step_fused",
+    "kda_fwd_chunked_fused", "kda_decode_step_fused", "attnres_forward", "attnres_forward_raw",
     "status_string", "version", "workspace_bytes",
 ]
 
@@ -33,7 +33,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
 # Every symbol include/kda.h declares.
 ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
                "kda_fwd_chunked_fused", "kda_fwd_chunked_workspace_bytes", "kda_decode_step",
-               "kda_decode_step_ex", "kda_decode_step_fused")
+               "kda_decode_step_ex", "kda_decode_step_fused", "attnres_forward")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.kda_fwd_chunked_fused.restype = i
         L.kda_decode_step_fused.argtypes = [vp, vp, vp, vp, vp, f, vp, vp, i, i, i, i, i, i, i, vp]
         L.kda_decode_step_fused.restype = i
+        L.attnres_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.attnres_forward.restype = i
         _lib = L
     return _lib
 
@@ -341,3 +343,31 @@ def kda_decode_step_fused(q_raw, k_raw, v, g_raw, b_raw, S, *, gate_scale: float
     if st != 0:
         raise KdaError(st, "kda_decode_step_fused")
     return o
+
+
+def attnres_forward_raw(q, k, h, out, L, N, d_k, d, dtype, stream=None) -> int:
+    return int(lib().attnres_forward(q, k, h, out, L, N, d_k, d, dtype, stream))
+
+
+def attnres_forward(q, k, h, *, out=None):
+    """AttnRes depth aggregation: out[n] = sum_i softmax_i(q[n] . k[i, n]) h[i, n].
+    q [N,d_k], k [L,N,d_k], h [L,N,d] (bf16 or fp32, one dtype).  Returns out [N,d]."""
+    torch = _torch()
+    if k.dim() != 3 or h.dim() != 3:
+        raise ValueError("k must be [L,N,d_k] and h [L,N,d]")
+    L, N, d_k = k.shape
+    d = h.shape[-1]
+    dt, dev = q.dtype, q.device
+    code = _dtype_code(q)
+    _check(q, "q", (N, d_k), dt, dev)
+    _check(k, "k", (L, N, d_k), dt, dev)
+    _check(h, "h", (L, N, d), dt, dev)
+    if out is None:
+        out = torch.empty((N, d), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, d), dt, dev)
+    st = attnres_forward_raw(q.data_ptr(), k.data_ptr(), h.data_ptr(), out.data_ptr(), L, N, d_k, d,
+                             code, _stream_handle(dev))
+    if st != 0:
+        raise KdaError(st, "attnres_forward")
+    return out

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "attnres.hip"]
 
 # -packed-fp32-ops off: every fp32 op stays scalar VALU (no v_pk_*_f32).
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",

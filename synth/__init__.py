@@ -253,3 +253,17 @@ def raw_prefill_inputs(B: int, T: int, H: int, d_k: int, d_v: int, *, dtype: str
         out = {n: round_to_bf16(a) for n, a in out.items()}
     out["S0"] = (s0_std * rng.standard_normal((B, H, d_k, d_v))).astype(np.float32) if s0_std > 0 else None
     return out
+
+
+def attnres_inputs(L: int, N: int, d_k: int, d: int, *, dtype: str = "bf16", seed: int = 0) -> dict:
+    """AttnRes inputs: q [N,d_k], k [L,N,d_k] ~ N(0, 1/sqrt(d_k)) each (so a
+    score q.k has unit variance), h [L,N,d] ~ N(0,1); float32, bf16-exact when
+    dtype == "bf16"."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 4242])))
+    s = d_k ** -0.25
+    out = {"q": (s * rng.standard_normal((N, d_k))).astype(np.float32),
+           "k": (s * rng.standard_normal((L, N, d_k))).astype(np.float32),
+           "h": rng.standard_normal((L, N, d), dtype=np.float32)}
+    if dtype == "bf16":
+        out = {n: round_to_bf16(a) for n, a in out.items()}
+    return out

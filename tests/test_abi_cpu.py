@@ -11,8 +11,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _header_symbols():
-    txt = open(os.path.join(ROOT, "include", "kda.h")).read()
-    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", txt)))
+    syms = set()
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            txt = open(os.path.join(inc, f)).read()
+            syms |= set(re.findall(r"^KDA_API\s+[\w\s\*]*?\b(\w+)\s*\(", txt, re.M))
+    return sorted(syms)
 
 
 def test_header_declares_the_abi():
@@ -180,3 +185,16 @@ def test_decode_fused_validation():
                                          0, 0) == 1
     assert kda.kda_decode_step_fused_raw(P, P, P, None, P, 0.1, P, P, 2, 2, 128, 128, kda.KDA_BF16,
                                          1, 0) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(L=0), 1), (dict(N=0), 1), (dict(dtype=5), 1),
+    (dict(L=2000), 2), (dict(d=12), 2), (dict(d_k=600), 2), (dict(h=P + 8), 1),
+    (dict(out=P), 1),                                   # out overlaps the inputs
+])
+def test_attnres_validation(kw, code):
+    a = dict(q=P, k=P + (1 << 24), h=P + (2 << 24), out=P + (3 << 24), L=4, N=8, d_k=16, d=64,
+             dtype=kda.KDA_BF16)
+    a.update(kw)
+    assert kda.attnres_forward_raw(a["q"], a["k"], a["h"], a["out"], a["L"], a["N"], a["d_k"], a["d"],
+                                   a["dtype"]) == code
