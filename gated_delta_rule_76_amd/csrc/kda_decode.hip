@@ -30,7 +30,7 @@ namespace {
 template <int DK, int DV>
 struct DecodeShape {
   static constexpr int CG = DV / 4;                              // float4 column groups
-  static constexpr int NTH = (DK * CG < 256) ? DK * CG : 256;    // threads per workgroup
+  static constexpr int NTH = (DK * CG < 512) ? DK * CG : 512;    // threads per workgroup
   static constexpr int RG = NTH / CG;                            // row groups
   static constexpr int RPT = DK / RG;                            // rows per thread
   static constexpr int NW = NTH / 64;                            // waves
