@@ -202,3 +202,75 @@ def test_decode_alpha_zero_exact():
     o_ref = (bb * np.sum(kk * qq, -1))[..., None] * vv
     assert rel_err(S.cpu().numpy(), S_ref) <= 1e-6
     assert rel_err(to_np(o), o_ref) <= 1e-6
+
+
+# ---------------------------------------------------------------- variants
+@pytest.mark.parametrize("gate,rule", [("head", "delta"), ("none", "delta"), ("channel", "linear"),
+                                       ("head", "linear")])
+def test_variant_decode_steps_match_prefill(gate, rule):
+    import torch
+    kda = _kda()
+    log(f"[decode == prefill] gate={gate} rule={rule} bf16 dk128 dv64 T30")
+    T = 30
+    x = prefill_inputs(2, T, 2, 128, 64, dtype="bf16", seed=31)
+    q, k, v, a, b = _dev_inputs(x, "bf16")
+    if gate == "head":
+        a = a[..., 0].contiguous()
+    elif gate == "none":
+        a = None
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o_pre, s_pre = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=16, gate=gate, rule=rule)
+    S = s0.clone()
+    outs = []
+    for t in range(T):
+        at = None if a is None else a[:, t].contiguous()
+        outs.append(kda.kda_decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                        at, b[:, t].contiguous(), S, gate=gate, rule=rule))
+    torch.cuda.synchronize()
+    assert rel_err(to_np(torch.stack(outs, dim=1)), to_np(o_pre)) <= 2 * TOL["bf16"]
+    assert rel_err(to_np(S), to_np(s_pre)) <= 2 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("gate,rule", [("head", "delta"), ("channel", "linear")])
+def test_variant_split_resume_aligned_is_bitwise(gate, rule):
+    import torch
+    kda = _kda()
+    log(f"[split/resume] gate={gate} rule={rule} bf16 C64")
+    T1, T2 = 128, 133
+    x = prefill_inputs(1, T1 + T2, 2, 128, 128, dtype="bf16", seed=32)
+    q, k, v, a, b = _dev_inputs(x, "bf16")
+    if gate == "head":
+        a = a[..., 0].contiguous()
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    kw = dict(chunk=64, gate=gate, rule=rule)
+    o_all, s_all = kda.kda_fwd_chunked(q, k, v, a, b, s0, **kw)
+    sl = lambda t, lo, hi: t[:, lo:hi].contiguous()
+    o1, s1 = kda.kda_fwd_chunked(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(a, 0, T1), sl(b, 0, T1), s0, **kw)
+    o2, s2 = kda.kda_fwd_chunked(sl(q, T1, None), sl(k, T1, None), sl(v, T1, None), sl(a, T1, None),
+                                 sl(b, T1, None), s1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[:, :T1], o1) and torch.equal(o_all[:, T1:], o2)
+    assert torch.equal(s_all, s2)
+
+
+def test_fused_prologue_on_unit_inputs_matches_plain_path():
+    # Raw inputs that the maps leave unchanged up to fp32 rounding: already
+    # unit q, k; gate and beta pre-activations chosen through the inverse maps.
+    # The fused path must then agree with the plain path to the bf16 bound.
+    import torch
+    kda = _kda()
+    log("[fused == plain] bf16 dk128 dv128 C64 T150")
+    x = prefill_inputs(1, 150, 2, 128, 128, dtype="f32", gate_c=0.1, seed=33)
+    c = 0.1
+    # inverse maps (computed in fp64 on the host): alpha = exp(-c softplus(g)) -> g; beta = sigmoid(b) -> b
+    sp = -np.log(x["alpha"].astype(np.float64)) / c
+    g = np.log(np.expm1(sp))
+    bb = np.log(x["beta"] / (1.0 - x["beta"]))
+    dev = lambda a: to_dev(round_to_bf16(np.asarray(a, dtype=np.float32)), "bf16")
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    o_f, s_f = kda.kda_fwd_chunked_fused(q, k, v, dev(g), dev(bb), s0, gate_scale=c, chunk=64)
+    o_p, s_p = kda.kda_fwd_chunked(q, k, v, dev(x["alpha"]), dev(x["beta"]), s0, chunk=64)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(o_f), to_np(o_p)) <= TOL["bf16"]
+    assert rel_err(to_np(s_f), to_np(s_p)) <= TOL["bf16"]
