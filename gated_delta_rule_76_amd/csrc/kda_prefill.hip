@@ -35,8 +35,9 @@
 //     Gram products on the matrix cores, inverts the unit lower-triangular
 //     system in fp32, and writes five operand tiles (K+, Q+, Kbar^T, Tm, P)
 //     plus gamma_C into a workspace slot, already in the per-lane order the
-//     MFMA operands need.  Each workgroup walks a strided list of chunks and
-//     prefetches the next chunk's inputs into registers while it works.
+//     MFMA operands need (streaming stores: nothing re-reads them from L2
+//     soon).  Each workgroup walks a strided list of chunks and prefetches
+//     the next chunk's inputs into registers while it works.
 //   state_pass_kernel: one workgroup per (batch, head, value block), one
 //     wave per 16-column slab of the fp32 state, which lives in accumulator
 //     registers for the whole sequence.  It walks the chunks in order; the
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
             half_acc[hh] = acc;
           }
           frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (S::tri(tr) + s2) * S::FRAG);
-          dst[lane] = M::from_acc(half_acc[0], half_acc[1]);
+          __builtin_nontemporal_store(M::from_acc(half_acc[0], half_acc[1]), &dst[lane]);
         }
       // K+ and Q+ fragments: rows r, k = channels.
       constexpr int NKQ = 2 * S::NT * S::NKS;
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         const lds_t* row = (w2 ? Qp : Kp) + (16 * t + c16) * P::LDK;
         const int kb = 32 * s2 + 4 * g;
         const frag f = (S::KODD && s2 == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
-        reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane] = f;
+        __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane]);
       }
       // Kbar^T fragments: rows = channels 16t + c16, k = token rows, gathered
       // down a column of the row-major Kbar tile.
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) f[4 + e] = colp[(r0 + 16 + e) * P::LDK];
         }
-        reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane] = f;
+        __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane]);
       }
       if (tid < DK) reinterpret_cast<float*>(slot + S::OFF_GC)[tid] = sm.gC[tid];
     }
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
             for (int e = 0; e < 4; ++e) t8[4 + e] = kb + 16 + e <= r ? hi[e] * sm.beta[kb + 16 + e] : 0.f;
           }
           frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (S::tri(tr) + s2) * S::FRAG);
-          dst[lane] = M::from8(t8);
+          __builtin_nontemporal_store(M::from8(t8), &dst[lane]);
         }
     }
   }
