@@ -360,6 +360,8 @@ def main():
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(aby / (a_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                                 "alg_bytes_per_launch": aby,
+                                "traffic": _recorded_traffic("attnres.hip",
+                                                             "attnres_l64_n4096_d4096_counters.txt"),
                                 "launch": "one attnres_forward call: attnres_kernel"}}
 
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample_tokens)
