@@ -53,6 +53,7 @@
 // in this order, one 16-byte (bf16) or 32-byte (fp32) fragment per lane.
 // The reduction does not depend on which k each (lane, element) slot
 // carries as long as both operands agree.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -984,13 +985,19 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  static bool attr_set = false;  // one-time opt-in to more than 64 KiB of LDS
-  if (!attr_set) {
+  // Opt in to more than 64 KiB of LDS, once per device (bit d of the mask;
+  // devices past 63 opt in on every launch).
+  static std::atomic<unsigned long long> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
     const void* fn = reinterpret_cast<const void*>(&state_pass_kernel<E, DK, DVB, C>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(K::smem_bytes));
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(K::smem_bytes));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   // grid.x = (batch, head) chains, grid.y = value blocks: the value blocks
   // of one chain are gridDim.x apart in dispatch order, which keeps them on
