@@ -67,6 +67,55 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lvoid_t;
 
 // ----------------------------------------------------------------- helpers
+// Batched LDS reads for the state chain: 16-byte reads at addr + offsets
+// issued back to back, then a single wait for all of them.  One asm
+// statement each, so that the compiler neither places a wait between the
+// reads nor moves them next to their uses (which serialises one LDS round
+// trip per matrix product).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+// 16 reads at addr + O + i * D, i = 0..15
+template <int O, int D>
+__device__ __forceinline__ void lds_read16(uint32_t a, u32x4 (&r)[16]) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%17\n\tds_read_b128 %1, %16 offset:%18\n\t"
+      "ds_read_b128 %2, %16 offset:%19\n\tds_read_b128 %3, %16 offset:%20\n\t"
+      "ds_read_b128 %4, %16 offset:%21\n\tds_read_b128 %5, %16 offset:%22\n\t"
+      "ds_read_b128 %6, %16 offset:%23\n\tds_read_b128 %7, %16 offset:%24\n\t"
+      "ds_read_b128 %8, %16 offset:%25\n\tds_read_b128 %9, %16 offset:%26\n\t"
+      "ds_read_b128 %10, %16 offset:%27\n\tds_read_b128 %11, %16 offset:%28\n\t"
+      "ds_read_b128 %12, %16 offset:%29\n\tds_read_b128 %13, %16 offset:%30\n\t"
+      "ds_read_b128 %14, %16 offset:%31\n\tds_read_b128 %15, %16 offset:%32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+        "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a), "i"(O), "i"(O + D), "i"(O + 2 * D), "i"(O + 3 * D), "i"(O + 4 * D), "i"(O + 5 * D),
+        "i"(O + 6 * D), "i"(O + 7 * D), "i"(O + 8 * D), "i"(O + 9 * D), "i"(O + 10 * D), "i"(O + 11 * D),
+        "i"(O + 12 * D), "i"(O + 13 * D), "i"(O + 14 * D), "i"(O + 15 * D)
+      : "memory");
+}
+// 6 reads at a + O + i * D and 8 reads at b + P + i * E
+template <int O, int D, int P, int E>
+__device__ __forceinline__ void lds_read6_8(uint32_t a, u32x4 (&r)[6], uint32_t b, u32x4 (&s)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %14 offset:%16\n\tds_read_b128 %1, %14 offset:%17\n\t"
+      "ds_read_b128 %2, %14 offset:%18\n\tds_read_b128 %3, %14 offset:%19\n\t"
+      "ds_read_b128 %4, %14 offset:%20\n\tds_read_b128 %5, %14 offset:%21\n\t"
+      "ds_read_b128 %6, %15 offset:%22\n\tds_read_b128 %7, %15 offset:%23\n\t"
+      "ds_read_b128 %8, %15 offset:%24\n\tds_read_b128 %9, %15 offset:%25\n\t"
+      "ds_read_b128 %10, %15 offset:%26\n\tds_read_b128 %11, %15 offset:%27\n\t"
+      "ds_read_b128 %12, %15 offset:%28\n\tds_read_b128 %13, %15 offset:%29\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(s[0]),
+        "=&v"(s[1]), "=&v"(s[2]), "=&v"(s[3]), "=&v"(s[4]), "=&v"(s[5]), "=&v"(s[6]), "=&v"(s[7])
+      : "v"(a), "v"(b), "i"(O), "i"(O + D), "i"(O + 2 * D), "i"(O + 3 * D), "i"(O + 4 * D),
+        "i"(O + 5 * D), "i"(P), "i"(P + E), "i"(P + 2 * E), "i"(P + 3 * E), "i"(P + 4 * E),
+        "i"(P + 5 * E), "i"(P + 6 * E), "i"(P + 7 * E)
+      : "memory");
+}
+
 template <typename St>
 struct Raw8;  // 8 consecutive token-tensor elements as loaded from memory
 template <>
@@ -671,7 +720,6 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool copier = wave >= K::NCW && wave < K::NCW + K::NCP;
   const bool storer = wave == K::NCW + K::NCP;
-  const bool fetcher = wave == K::NCW + K::NCP + 1;
   const int cw = wave - K::NCW;  // copy-wave index
   const long rs = static_cast<long>(H) * DV;  // element stride between tokens
   const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
@@ -736,7 +784,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   // State wave of slab j (wave j) holds Sa[ti] = S[16 ti + 4 g + e][col] in
   // accumulator registers; output wave of slab j is wave NSLAB + j.
   const int c16 = lane & 15, g = lane >> 4;
-  const bool stater = wave < K::NSLAB;
+  const bool stater = wave < K::NSLAB, outer = !stater && wave < K::NCW;
   const int slab = stater ? wave : wave - K::NSLAB;
   const int col = vb * DVB + 16 * slab + c16;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -744,9 +792,18 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   frag* xu = reinterpret_cast<frag*>(lds + K::OFF_XU) + slab * S::NCS * 64;
   int* flag = reinterpret_cast<int*>(lds + K::OFF_FLAG) + slab;
   constexpr int XSF = K::XS / S::FRAG * 64;  // frag elements per state buffer
-  f32x4 Sa[S::NTK];
-  frag sfr[S::NKS];  // bf16 (or fp32) operand copy of the state entering the chunk
+  auto slot_of = [&](int n) -> const char* { return lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT; };
+
+  // Each role runs its own loop over the chunks, so the register allocator
+  // sees one role's values at a time.  Every wave passes the same workgroup
+  // barriers in the same order: [A] at the top of each chunk, [B] after the
+  // compute waves are done with a single slot buffer (only when the slot is
+  // not double-buffered), and one final [A].  The store and prefetch waves
+  // pass them without draining their memory operations: nothing in the
+  // workgroup waits on those.
   if (stater) {
+    f32x4 Sa[S::NTK];
+    frag sfr[S::NKS];  // bf16 (or fp32) operand copy of the state entering the chunk
     if (S0 != nullptr) {
       const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
@@ -763,69 +820,74 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       xs[s2 * 64 + lane] = sfr[s2];
     }
     if (lane == 0) *flag = 0;
-  } else if (copier && nchunk > 0) {
-    stage_slot(0, 0);
-    stage_v(0);
-    __builtin_amdgcn_s_waitcnt(0);
-  } else if (fetcher && nchunk > 1) {
-    prefetch(1);
-  }
 
-  for (int n = 0; n < nchunk; ++n) {
-    const int t0 = n * C;
-    // [A].  The store wave passes it without draining its global stores:
-    // nothing in the workgroup waits on them.
-    if (storer || fetcher)
-      __builtin_amdgcn_s_barrier();
-    else
-      __syncthreads();
-    const char* sl = lds + (K::NBUF == 2 ? (n & 1) : 0) * K::SLOT;
-    auto fr = [&](int off, int idx) -> frag {
-      return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
-    };
-    if (storer) {
-      if (n > 0) store_out(n - 1);  // its LDS reads complete before the stores issue
-    } else if (fetcher) {
-      if (n + 2 < nchunk) {
-        __builtin_amdgcn_s_waitcnt(0);  // the previous chunk's prefetch has landed
-        prefetch(n + 2);
-      }
-    } else if (copier) {
-      if (n + 1 < nchunk) {
-        if (K::NBUF == 2) stage_slot(n + 1, (n + 1) & 1);
-        stage_v(n + 1);
-      }
-      if (K::NBUF == 2) __builtin_amdgcn_s_waitcnt(0);
-    } else if (stater) {
-      // Each product first issues all of its LDS operand reads, then runs its
-      // MFMAs with the independent accumulator chains interleaved (k-step
-      // outermost), so the matrix pipe is not waiting on one chain.
+    // One chunk of the chain, straight-line per update rule.  For bf16 at
+    // d_k = 128, C = 64 the operand reads of each product group go out as
+    // one batch with a single LDS wait (see lds_read16).
+    constexpr bool FAST = std::is_same<E, Bf16>::value && S::NT * S::NKS == 16 && S::NTRI == 6 &&
+                          S::NTK == 8 && S::NTK * S::NCS == 16 && S::FRAG == 1024;
+    auto chain_step = [&](int n, auto delta_rule) {
+      constexpr bool DELTA = decltype(delta_rule)::value;
+      const int t0 = n * C;
+      const char* sl = slot_of(n);
+      auto fr = [&](int off, int idx) -> frag {
+        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
+      };
+      const uint32_t fb = lds_addr(sl) + 16 * lane, gb = lds_addr(sl) + 16 * g;
       const St* vt = reinterpret_cast<const St*>(lds + K::OFF_V + (n & 1) * K::VTILE);
       const float* gC = reinterpret_cast<const float*>(sl + S::OFF_GC);
-      frag akp[S::NT][S::NKS];
-#pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr)
-#pragma unroll
-        for (int s2 = 0; s2 < S::NKS; ++s2) akp[tr][s2] = fr(S::OFF_KP, tr * S::NKS + s2);
-      float vr[S::NT][4];
-#pragma unroll
-      for (int tr = 0; tr < S::NT; ++tr)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16);
 
       // R = V - K+ S  (R = V without the correction)
       f32x4 R[S::NT];
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr) R[tr] = z;
-      if (rule == kRuleDelta) {
+      if constexpr (DELTA) {
+        frag akp[S::NT][S::NKS];
+        if constexpr (FAST) {
+          u32x4 r[16];
+          lds_read16<S::OFF_KP, S::FRAG>(fb, r);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) akp[i / S::NKS][i % S::NKS] = __builtin_bit_cast(frag, r[i]);
+        } else {
+#pragma unroll
+          for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+            for (int s2 = 0; s2 < S::NKS; ++s2) akp[tr][s2] = fr(S::OFF_KP, tr * S::NKS + s2);
+        }
+        // the independent accumulator chains interleaved (k-step outermost)
 #pragma unroll
         for (int s2 = 0; s2 < S::NKS; ++s2)
 #pragma unroll
           for (int tr = 0; tr < S::NT; ++tr) R[tr] = M::mma(akp[tr][s2], sfr[s2], R[tr]);
       }
       frag atm[S::NTRI];
+      f32x4 gcv[S::NTK];
+      if constexpr (FAST) {
+        u32x4 r[6], q[8];
+        lds_read6_8<S::OFF_TM, S::FRAG, S::OFF_GC, 64>(fb, r, gb, q);
 #pragma unroll
-      for (int i = 0; i < S::NTRI; ++i) atm[i] = fr(S::OFF_TM, i);
+        for (int i = 0; i < 6; ++i) atm[i] = __builtin_bit_cast(frag, r[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gcv[i] = __builtin_bit_cast(f32x4, q[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < S::NTRI; ++i) atm[i] = fr(S::OFF_TM, i);
+#pragma unroll
+        for (int ti = 0; ti < S::NTK; ++ti) gcv[ti] = *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
+      }
+      // Diag(gamma_C) S on the fp32 state (R used the operand copy of the
+      // state entering the chunk); kept here so that gamma_C is dead before
+      // the next operands arrive
+#pragma unroll
+      for (int ti = 0; ti < S::NTK; ++ti) {
+        Sa[ti] *= gcv[ti];
+        asm volatile("" : "+v"(Sa[ti]));
+      }
+      float vr[S::NT][4];
+#pragma unroll
+      for (int tr = 0; tr < S::NT; ++tr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16);
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
@@ -844,10 +906,17 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
         for (int tr = 2 * s2; tr < S::NT; ++tr) U[tr] = M::mma(atm[S::tri(tr) + s2], rfr[s2], U[tr]);
       frag akb[S::NTK][S::NCS];
+      if constexpr (FAST) {
+        u32x4 r[16];
+        lds_read16<S::OFF_KB, S::FRAG>(fb, r);
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti)
+        for (int i = 0; i < 16; ++i) akb[i / S::NCS][i % S::NCS] = __builtin_bit_cast(frag, r[i]);
+      } else {
 #pragma unroll
-        for (int s2 = 0; s2 < S::NCS; ++s2) akb[ti][s2] = fr(S::OFF_KB, ti * S::NCS + s2);
+        for (int ti = 0; ti < S::NTK; ++ti)
+#pragma unroll
+          for (int s2 = 0; s2 < S::NCS; ++s2) akb[ti][s2] = fr(S::OFF_KB, ti * S::NCS + s2);
+      }
       frag ufr[S::NCS];
 #pragma unroll
       for (int s2 = 0; s2 < S::NCS; ++s2) {
@@ -859,8 +928,6 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 
       // S <- Diag(gamma_C) S + Kbar^T U
 #pragma unroll
-      for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] *= *reinterpret_cast<const f32x4*>(gC + 16 * ti + 4 * g);
-#pragma unroll
       for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
         for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = M::mma(akb[ti][s2], ufr[s2], Sa[ti]);
@@ -871,8 +938,35 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
         sfr[s2] = M::from_acc(Sa[2 * s2], (S::KODD && s2 == S::NKS - 1) ? z : Sa[2 * s2 + 1]);
         xn[s2 * 64 + lane] = sfr[s2];
       }
-    } else {
-      // Output wave: O = Q+ S_in + P U into the output tile.
+    };
+    // one loop per update rule, so that neither shares code with the other
+    auto run_chain = [&](auto delta_rule) {
+      for (int n = 0; n < nchunk; ++n) {
+        __syncthreads();  // [A]
+        chain_step(n, delta_rule);
+        if (K::NBUF == 1) __syncthreads();  // [B]
+      }
+    };
+    if (rule == kRuleDelta)
+      run_chain(std::true_type{});
+    else
+      run_chain(std::false_type{});
+    if (nchunk > 0) __syncthreads();  // final [A]
+    if (ST != nullptr) {
+      float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+#pragma unroll
+      for (int ti = 0; ti < S::NTK; ++ti)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
+    }
+  } else if (outer) {
+    // Output wave: O = Q+ S_in + P U into the output tile.
+    for (int n = 0; n < nchunk; ++n) {
+      __syncthreads();  // [A]
+      const char* sl = slot_of(n);
+      auto fr = [&](int off, int idx) -> frag {
+        return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
+      };
       St* ot = reinterpret_cast<St*>(lds + K::OFF_O + (n & 1) * K::VTILE);
       const frag* xc = xs + (n & 1) * XSF;
       frag osf[S::NKS], aqp[S::NT][S::NKS];
@@ -909,33 +1003,53 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
         for (int e = 0; e < 4; ++e) store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16, O[tr][e]);
+      if (K::NBUF == 1) __syncthreads();  // [B]
     }
-    if (K::NBUF == 1) {
-      if (storer || fetcher)
-        __builtin_amdgcn_s_barrier();
-      else
-        __syncthreads();  // every compute wave is done with the single slot
-      if (copier) {
+    if (nchunk > 0) __syncthreads();  // final [A]
+  } else if (copier) {
+    if (nchunk > 0) {
+      stage_slot(0, 0);
+      stage_v(0);
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    for (int n = 0; n < nchunk; ++n) {
+      __syncthreads();  // [A]
+      if (n + 1 < nchunk) {
+        if (K::NBUF == 2) stage_slot(n + 1, (n + 1) & 1);
+        stage_v(n + 1);
+      }
+      if (K::NBUF == 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+      } else {
+        __syncthreads();  // [B]: every compute wave is done with the single slot
         if (n + 1 < nchunk) stage_slot(n + 1, 0);
         __builtin_amdgcn_s_waitcnt(0);
       }
     }
-  }
-  if (nchunk > 0) {
-    if (storer || fetcher)
-      __builtin_amdgcn_s_barrier();
-    else
-      __syncthreads();  // the last output tile is in LDS
-    if (storer) store_out(nchunk - 1);
-  }
-  if (storer || fetcher) __builtin_amdgcn_s_waitcnt(0);
-
-  if (stater && ST != nullptr) {
-    float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
-#pragma unroll
-    for (int ti = 0; ti < S::NTK; ++ti)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
+    if (nchunk > 0) __syncthreads();  // final [A]
+  } else if (storer) {
+    for (int n = 0; n < nchunk; ++n) {
+      __builtin_amdgcn_s_barrier();  // [A]
+      if (n > 0) store_out(n - 1);   // its LDS reads complete before the stores issue
+      if (K::NBUF == 1) __builtin_amdgcn_s_barrier();  // [B]
+    }
+    if (nchunk > 0) {
+      __builtin_amdgcn_s_barrier();  // final [A]: the last output tile is in LDS
+      store_out(nchunk - 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {  // prefetch wave
+    if (nchunk > 1) prefetch(1);
+    for (int n = 0; n < nchunk; ++n) {
+      __builtin_amdgcn_s_barrier();  // [A]
+      if (n + 2 < nchunk) {
+        __builtin_amdgcn_s_waitcnt(0);  // the previous chunk's prefetch has landed
+        prefetch(n + 2);
+      }
+      if (K::NBUF == 1) __builtin_amdgcn_s_barrier();  // [B]
+    }
+    if (nchunk > 0) __builtin_amdgcn_s_barrier();  // final [A]
+    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 
