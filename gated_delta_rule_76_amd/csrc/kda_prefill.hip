@@ -122,9 +122,12 @@ template <>
 struct Raw8<uint16_t> {
   uint4 r;
   __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void splat(const uint16_t* p) {  // one value in all 8 slots
-    const unsigned w = static_cast<unsigned>(*p) * 0x10001u;
-    r = uint4{w, w, w, w};
+  // one value for all 8 slots: loaded here, broadcast by unpack_one (so the
+  // load is not waited for until the value is used)
+  __device__ __forceinline__ void load_one(const uint16_t* p) { r.x = *p; }
+  __device__ __forceinline__ f32x8 unpack_one() const {
+    const float x = __uint_as_float(r.x << 16);
+    return f32x8{x, x, x, x, x, x, x, x};
   }
   __device__ __forceinline__ void ones() { r = uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}; }
   __device__ __forceinline__ f32x8 unpack() const {
@@ -143,10 +146,10 @@ struct Raw8<float> {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
   }
-  __device__ __forceinline__ void splat(const float* p) {
-    const float x = *p;
-    a = f32x4{x, x, x, x};
-    b = a;
+  __device__ __forceinline__ void load_one(const float* p) { a.x = *p; }
+  __device__ __forceinline__ f32x8 unpack_one() const {
+    const float x = a.x;
+    return f32x8{x, x, x, x, x, x, x, x};
   }
   __device__ __forceinline__ void ones() { a = b = f32x4{1.f, 1.f, 1.f, 1.f}; }
   __device__ __forceinline__ f32x8 unpack() const { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
@@ -282,14 +285,21 @@ struct PrepCfg {
                                      : SCAN);
   static constexpr int OFF_KP = 0, OFF_KM = TILE, OFF_QP = 2 * TILE, OFF_KB = 3 * TILE;
   static constexpr int OFF_MF = 0, OFF_XF = MF, OFF_SCAN = 0;
+  // Tm fragments are staged for a delayed write when they fit next to the
+  // rest (two workgroups per CU); otherwise they are written directly.
+  static constexpr int TMB = S::NTRI * S::FRAG;
+  static constexpr bool STAGE_TM = REGION + 4 * DK + 4 * C + TMB <= 80 * 1024;
   struct Smem {
     alignas(16) char region[REGION];
     alignas(16) float gC[DK];
     alignas(16) float beta[C];
+    alignas(16) char tm[STAGE_TM ? TMB : 16];
   };
 };
 
-template <typename E, int DK, int C>
+// CHANNEL: per-channel gate (the KDA case), compiled without the gate-kind
+// branches around the input loads; otherwise the gate kind is read at run time.
+template <typename E, int DK, int C, bool CHANNEL>
 __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ alpha, const typename E::storage* __restrict__ beta,
@@ -301,6 +311,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   using lds_t = typename S::lds_t;
   using frag = typename S::frag;
   using St = typename E::storage;
+  if constexpr (CHANNEL) gate = kGateChannel;
   __shared__ typename P::Smem sm;
   lds_t* const Kp = reinterpret_cast<lds_t*>(sm.region + P::OFF_KP);
   lds_t* const Km = reinterpret_cast<lds_t*>(sm.region + P::OFF_KM);
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
           if (gate == kGateChannel)
             ra[rr].load(alpha + row * DK + ch0);
           else if (gate == kGateHead)
-            ra[rr].splat(alpha + row);  // one decay for every channel of the head
+            ra[rr].load_one(alpha + row);  // one decay for every channel of the head
           else
             ra[rr].ones();
           rk[rr].load(k + row * DK + ch0);
@@ -350,6 +361,24 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     }
   };
   prefetch(blockIdx.x);
+
+  // The Tm fragments of a task are staged in LDS and written out early in
+  // the next task, right behind the other stores: a wave's loads and stores
+  // retire in issue order, so a store issued at the very end of a task would
+  // hold up the next task's first use of its prefetched inputs.
+  char* tm_slot = nullptr;  // slot whose Tm fragments are staged
+  auto flush_tm = [&]() {
+    if (P::STAGE_TM && tm_slot != nullptr) {
+      // the lane offset (lane * fragment bytes per lane) is recomputed here
+      // rather than kept live across tasks
+      static_assert(S::FB == 16 || S::FB == 32, "lane fragment bytes");
+      uint32_t lo;
+      asm volatile("v_lshlrev_b32 %0, %2, %1" : "=v"(lo) : "v"(lane), "i"(S::FB == 16 ? 4 : 5));
+      for (int i = wave; i < S::NTRI; i += NW_PREP)
+        __builtin_nontemporal_store(*reinterpret_cast<const frag*>(sm.tm + i * S::FRAG + lo),
+                                    reinterpret_cast<frag*>(tm_slot + S::OFF_TM + i * S::FRAG + lo));
+    }
+  };
 
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
     const int n = task / nchain;
@@ -366,7 +395,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
       for (int rr = 0; rr < P::RPG; ++rr) {
         const bool ok = rg * P::RPG + rr < valid;
-        f32x8 a = ra[rr].unpack();
+        f32x8 a = gate == kGateHead ? ra[rr].unpack_one() : ra[rr].unpack();
         if (fused && gate != kGateNone) {  // raw gate projection -> decay
 #pragma unroll
           for (int e = 0; e < 8; ++e) a[e] = gate_map(a[e], gscale);
@@ -442,11 +471,15 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         M::store8(&Kb[r * P::LDK + ch0], kb);
       }
     }
-    prefetch(task + gridDim.x);  // next task's inputs load while this one computes
     __syncthreads();
 
     // ---- 3. Gram tiles (kept in registers), P fragments, and the K+ / Q+ /
-    //         Kbar^T fragments copied into the workspace slot
+    //         Kbar^T fragments copied into the workspace slot; first the
+    //         previous task's Tm fragments.  This task's inputs are all in
+    //         use by now: saying so here keeps the compiler from waiting on
+    //         this task's stores before the next prefetch reuses registers.
+    __builtin_amdgcn_s_waitcnt(0);
+    flush_tm();
     f32x4 Aacc[P::APW];
     {
       int job = 0;
@@ -538,6 +571,10 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       if (tid < DK) reinterpret_cast<float*>(slot + S::OFF_GC)[tid] = sm.gC[tid];
     }
     __syncthreads();  // the operand tiles are dead: Mf and Xf take their bytes
+    // The next task's inputs load while this one finishes.  Issued after
+    // this task's stores and before none, so the next task's first use of
+    // them waits only for stores that are long done.
+    prefetch(task + gridDim.x);
 
     // ---- 4. Mf = Diag(beta) strict_lower(A), then X = (I + Mf)^{-1}
     {
@@ -549,11 +586,12 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
           if (job % NW_PREP != wave) continue;
           const f32x4 acc = Aacc[job / NW_PREP];
           const int jc = 16 * tc + c16;
+          const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[16 * tr + 4 * g]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * tr + 4 * g + e;
             // without the correction there is no erase term: A = 0, Tm = Diag(beta)
-            Mf[r * P::LDF + jc] = jc < r && rule == kRuleDelta ? sm.beta[r] * acc[e] : 0.f;
+            Mf[r * P::LDF + jc] = jc < r && rule == kRuleDelta ? bt[e] * acc[e] : 0.f;
           }
         }
     }
@@ -634,10 +672,17 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) t8[4 + e] = kb + 16 + e <= r ? hi[e] * sm.beta[kb + 16 + e] : 0.f;
           }
-          frag* dst = reinterpret_cast<frag*>(slot + S::OFF_TM + (S::tri(tr) + s2) * S::FRAG);
-          __builtin_nontemporal_store(M::from8(t8), &dst[lane]);
+          if constexpr (P::STAGE_TM)
+            reinterpret_cast<frag*>(sm.tm + (S::tri(tr) + s2) * S::FRAG)[lane] = M::from8(t8);
+          else
+            __builtin_nontemporal_store(M::from8(t8), &reinterpret_cast<frag*>(slot + S::OFF_TM + (S::tri(tr) + s2) * S::FRAG)[lane]);
         }
     }
+    tm_slot = slot;
+  }
+  if constexpr (P::STAGE_TM) {
+    __syncthreads();  // the last task's Tm fragments are staged
+    flush_tm();
   }
 }
 
@@ -1091,7 +1136,8 @@ hipError_t launch_t(const PrefillArgs& a) {
   if (ntask > 0) {
     // two resident workgroups per CU, each walking a strided list of chunks
     const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
-    hipLaunchKernelGGL((chunk_prep_kernel<E, DK, C>), dim3(grid), dim3(NTH_PREP), 0, a.stream,
+    auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
+    hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k),
                        static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
                        a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
