@@ -1125,26 +1125,12 @@ int num_cus() {
   return g_num_cus;
 }
 
-template <typename E, int DK, int DV, int C>
-hipError_t launch_t(const PrefillArgs& a) {
+// State pass with value blocks of DVB columns: one workgroup per (chain,
+// value block).
+template <typename E, int DK, int DVB, int C>
+hipError_t launch_pass(const PrefillArgs& a, const char* ws, int nchunk) {
   using St = typename E::storage;
-  constexpr int DVB = dvb_for(DV);
   using K = PassCfg<E, DK, DVB, C>;
-  const int nchunk = (a.T + C - 1) / C;
-  const long ntask = static_cast<long>(a.B) * a.H * nchunk;
-  char* ws = static_cast<char*>(a.workspace);
-  if (ntask > 0) {
-    // two resident workgroups per CU, each walking a strided list of chunks
-    const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
-    auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
-    hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
-                       static_cast<const St*>(a.q), static_cast<const St*>(a.k),
-                       static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
-                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
-                       a.gate_scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   // Opt in to more than 64 KiB of LDS, once per device (bit d of the mask;
   // devices past 63 opt in on every launch).
   static std::atomic<unsigned long long> attr_set{0};
@@ -1162,10 +1148,39 @@ hipError_t launch_t(const PrefillArgs& a) {
   // grid.x = (batch, head) chains, grid.y = value blocks: the value blocks
   // of one chain are gridDim.x apart in dispatch order, which keeps them on
   // one XCD (and its L2) whenever gridDim.x is a multiple of 8.
-  hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, DV / DVB),
+  hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, a.d_v / DVB),
                      dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
-                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, DV, nchunk, a.rule);
+                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, a.d_v, nchunk, a.rule);
   return hipGetLastError();
+}
+
+template <typename E, int DK, int DV, int C>
+hipError_t launch_t(const PrefillArgs& a) {
+  using St = typename E::storage;
+  const int nchunk = (a.T + C - 1) / C;
+  const long ntask = static_cast<long>(a.B) * a.H * nchunk;
+  char* ws = static_cast<char*>(a.workspace);
+  if (ntask > 0) {
+    // two resident workgroups per CU, each walking a strided list of chunks
+    const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
+    auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
+    hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
+                       static_cast<const St*>(a.q), static_cast<const St*>(a.k),
+                       static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
+                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
+                       a.gate_scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // The chain of each value block is sequential over the chunks.  When the
+  // 32-column blocks would leave more than half of the CUs idle (few long
+  // sequences), 16-column blocks put twice as many chains of work on the
+  // chip, each CU carrying one state slab instead of two.
+  if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit) {
+    if (static_cast<long>(a.B) * a.H * (DV / 32) * 2 <= num_cus())
+      return launch_pass<E, DK, 16, C>(a, ws, nchunk);
+  }
+  return launch_pass<E, DK, dvb_for(DV), C>(a, ws, nchunk);
 }
 
 template <typename E, int DK, int C>

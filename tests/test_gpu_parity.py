@@ -113,6 +113,11 @@ SHAPES = [
     ("bf16", 128, 64, 64, 2, 1, 2),
     ("bf16", 128, 128, 64, 1, 63, 1),
     ("bf16", 128, 128, 64, 1, 65, 1),
+    # enough (batch, head) chains that the state pass keeps 32-column value
+    # blocks on a 256-CU device (fewer chains take 16-column blocks)
+    ("bf16", 128, 128, 64, 4, 130, 10),
+    ("bf16", 64, 64, 32, 5, 99, 14),
+    ("f32", 64, 64, 32, 5, 70, 14),
 ]
 
 
