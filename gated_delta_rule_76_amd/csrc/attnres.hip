@@ -10,7 +10,7 @@
 //      max-subtracted) and leaves the weights in LDS
 //   3. weighted sum: each thread owns two groups of 8 adjacent columns per
 //      sweep of d and walks the layers four at a time (eight 16-byte row
-//      loads in flight), accumulating in fp32
+//      loads in flight, streaming), accumulating in fp32
 #include <math.h>
 #include <stdint.h>
 
@@ -23,12 +23,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxLayers = 1024;
 
+// The layer outputs are read once per call: streaming (nontemporal) loads
+// keep them from displacing other lines in the caches.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+
 template <typename St>
 struct Vec8;
 template <>
 struct Vec8<uint16_t> {  // 8 bf16 = 16 bytes
   uint4 r;
-  __device__ __forceinline__ void load(const uint16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    r = uint4{t[0], t[1], t[2], t[3]};
+  }
   __device__ __forceinline__ void fma(float w, float* acc) const {
     acc[0] += w * __uint_as_float(r.x << 16); acc[1] += w * __uint_as_float(r.x & 0xffff0000u);
     acc[2] += w * __uint_as_float(r.y << 16); acc[3] += w * __uint_as_float(r.y & 0xffff0000u);
@@ -48,8 +56,10 @@ template <>
 struct Vec8<float> {  // 8 fp32 = 32 bytes
   float4 a, b;
   __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const float4*>(p);
-    b = *reinterpret_cast<const float4*>(p + 4);
+    const f32x4_nt x = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+    const f32x4_nt y = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p + 4));
+    a = float4{x[0], x[1], x[2], x[3]};
+    b = float4{y[0], y[1], y[2], y[3]};
   }
   __device__ __forceinline__ void fma(float w, float* acc) const {
     acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
