@@ -95,27 +95,26 @@ def _upload(x, names, dtype):
 
 
 def _time_launches(fn, steps: int, warmup: int):
-    """Warm up, then time `steps` launches on torch's current stream (the
-    stream the library launches on).  Returns (total_s, per-launch ms list)."""
+    """Warm up, then time `steps` back-to-back launches on torch's current
+    stream (the stream the library launches on) with HIP events at the two
+    ends of the timed region, bracketed by device synchronisation.  Returns
+    (total seconds, average launch duration in ms = total / steps).  No events
+    sit between the launches: on an 80 us decode step they would add several
+    percent of measurement to the work."""
     import torch
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for a, b in ev:
-        a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return t_start.elapsed_time(t_end) / 1e3, per
+    total = t_start.elapsed_time(t_end) / 1e3
+    return total, total * 1e3 / steps
 
 
 def bench_prefill(name: str, steps: int, warmup: int, gate: str = "channel"):
@@ -290,7 +289,7 @@ def main():
     w, total, per, ok_p = bench_prefill(PREFILL, args.steps, args.warmup)
     tokens = w.B * w.T
     value = tokens * args.steps / total
-    launch_ms = sum(per) / len(per)
+    launch_ms = per
     by = prefill_alg_bytes(w.B, w.T, w.H, w.d_k, w.d_v)
     fl = prefill_alg_flops(w.B, w.T, w.H, w.d_k, w.d_v, w.chunk)
     gbs = by / (launch_ms / 1e3) / 1e9
@@ -306,7 +305,7 @@ def main():
     # ---- decode B256 H16, 1000 consecutive steps
     wd, dtot, dper, ok_d = bench_decode(args.decode_steps, 10)
     dby = decode_alg_bytes(wd.B, wd.H, wd.d_k, wd.d_v)
-    d_launch = sum(dper) / len(dper)
+    d_launch = dper
     d_gbs = dby / (d_launch / 1e3) / 1e9
     decode = {"value": round(dby * args.decode_steps / dtot / 1e9, 1), "unit": "GB/s",
               "steps": args.decode_steps, "ms_per_step": round(dtot * 1e3 / args.decode_steps, 4),
@@ -323,7 +322,7 @@ def main():
     long_ctx = None
     if not args.no_long:
         wl, ltot, lper, ok_l = bench_prefill(LONG, args.long_steps, 1)
-        l_ms = sum(lper) / len(lper)
+        l_ms = lper
         lby = prefill_alg_bytes(wl.B, wl.T, wl.H, wl.d_k, wl.d_v)
         long_ctx = {"value": round(wl.B * wl.T * args.long_steps / ltot, 1), "unit": "tokens/s",
                     "ms_per_call": round(l_ms, 3), "finite": ok_l,
@@ -335,7 +334,7 @@ def main():
     gdn = None
     if not args.no_gdn:
         wg, gtot, gper, ok_g = bench_prefill(PREFILL, args.steps, args.warmup, gate="head")
-        g_ms = sum(gper) / len(gper)
+        g_ms = gper
         gby = prefill_alg_bytes(wg.B, wg.T, wg.H, wg.d_k, wg.d_v, gate_per_channel=False)
         gdn = {"value": round(wg.B * wg.T * args.steps / gtot, 1), "unit": "tokens/s",
                "ms_per_call": round(g_ms, 4), "finite": ok_g, "gate": "head",
@@ -349,7 +348,7 @@ def main():
     attnres = None
     if not args.no_attnres:
         atot, aper, ok_a = bench_attnres(args.steps, args.warmup)
-        a_ms = sum(aper) / len(aper)
+        a_ms = aper
         c = ATTNRES
         aby = attnres_alg_bytes(c["L"], c["N"], c["d_k"], c["d"])
         attnres = {"value": round(c["N"] * args.steps / atot, 1), "unit": "tokens/s",
