@@ -259,7 +259,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--long-steps", type=int, default=5)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
