@@ -32,6 +32,24 @@ def test_determinism_bitwise():
     np.testing.assert_array_equal(s1, s2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_value_block_width_is_bitwise_invisible(dtype):
+    """Each (batch, head) chain is computed the same way whichever value-block
+    width the launch picks (32 columns when many chains fill the CUs, 16 when
+    few do; on a 256-CU device these 40 chains take 32 and the 4 take 16): the
+    same chains run in a 40-chain call and in a 4-chain call must agree
+    bitwise."""
+    B, H, T = 4, 10, 130
+    log(f"[value-block width] {dtype} dk128 dv128 C32 B{B} H{H} T{T} vs its first 4 heads")
+    x = prefill_inputs(B, T, H, 128, 128, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=31)
+    o_all, s_all = run_prefill(x, dtype, 32)
+    sub = {n: np.ascontiguousarray(x[n][:1, :, :4]) for n in ("q", "k", "v", "alpha", "beta")}
+    sub["S0"] = np.ascontiguousarray(x["S0"][:1, :4])
+    o_sub, s_sub = run_prefill(sub, dtype, 32)
+    np.testing.assert_array_equal(o_sub, o_all[:1, :, :4])
+    np.testing.assert_array_equal(s_sub, s_all[:1, :4])
+
+
 @pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 32)])
 def test_split_resume_aligned_is_bitwise(dtype, C):
     import torch
