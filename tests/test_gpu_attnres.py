@@ -44,3 +44,18 @@ def test_attnres_deterministic():
     b = kda.attnres_forward(q, k, h)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_attnres_tokens_are_independent():
+    """A token's output depends only on its own q, k_i and h_i: the first 7
+    tokens of a 50-token call equal a 7-token call on those tokens, bitwise."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    log("[attnres token independence] bf16 L40 N50 dk128 d1024 vs its first 7 tokens")
+    x = attnres_inputs(40, 50, 128, 1024, dtype="bf16", seed=11)
+    full = kda.attnres_forward(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["h"], "bf16"))
+    sub = kda.attnres_forward(to_dev(np.ascontiguousarray(x["q"][:7]), "bf16"),
+                              to_dev(np.ascontiguousarray(x["k"][:, :7]), "bf16"),
+                              to_dev(np.ascontiguousarray(x["h"][:, :7]), "bf16"))
+    torch.cuda.synchronize()
+    assert torch.equal(full[:7], sub)

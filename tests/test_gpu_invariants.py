@@ -50,6 +50,27 @@ def test_value_block_width_is_bitwise_invisible(dtype):
     np.testing.assert_array_equal(s_sub, s_all[:1, :4])
 
 
+def test_decode_heads_are_independent():
+    """The decode step treats each (batch, head) on its own: heads 0..2 of
+    batch entry 1 in a B=6, H=5 step equal a B=1, H=3 step on those heads,
+    bitwise, output and state."""
+    import torch
+    kda = _kda()
+    log("[decode head independence] bf16 dk128 dv128 B6 H5 vs batch 1, heads 0..2")
+    x = prefill_inputs(6, 1, 5, 128, 128, dtype="bf16", gate_c=0.05, s0_std=0.05, seed=41)
+    q, k, v, al, be = (x[n][:, 0] for n in ("q", "k", "v", "alpha", "beta"))
+    S = torch.from_numpy(np.ascontiguousarray(x["S0"], dtype=np.float32)).cuda()
+    o = kda.kda_decode_step(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                            to_dev(al, "bf16"), to_dev(be, "bf16"), S)
+    pick = lambda a: np.ascontiguousarray(a[1:2, :3])
+    S1 = torch.from_numpy(np.ascontiguousarray(x["S0"][1:2, :3], dtype=np.float32)).cuda()
+    o1 = kda.kda_decode_step(to_dev(pick(q), "bf16"), to_dev(pick(k), "bf16"), to_dev(pick(v), "bf16"),
+                             to_dev(pick(al), "bf16"), to_dev(pick(be), "bf16"), S1)
+    torch.cuda.synchronize()
+    assert torch.equal(o[1:2, :3], o1)
+    assert torch.equal(S[1:2, :3], S1)
+
+
 @pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 32)])
 def test_split_resume_aligned_is_bitwise(dtype, C):
     import torch
