@@ -178,3 +178,28 @@ def test_decode_fused_prologue(dtype, gate):
     es = rel_err(S.cpu().numpy(), Sref)
     log(f"  rel_err S after {steps} steps {es:.2e}")
     assert es <= TOL[dtype]
+
+
+def test_prefill_fused_prologue_32_column_blocks():
+    """The fused entry point with enough chains (40) that the state pass takes
+    32-column value blocks on a 256-CU device; the oracle checks two chains."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    B, T, H, c = 4, 2048, 10, 0.05
+    log(f"[prefill fused gate=channel bf16 dk128 dv128 C64 B{B} T{T} H{H}, oracle on 2 chains]")
+    x = raw_prefill_inputs(B, T, H, 128, 128, dtype="bf16", s0_std=0.01, seed=77)
+    q, k, v, g, b = (to_dev(x[n], "bf16") for n in ("q_raw", "k_raw", "v", "g_raw", "b_raw"))
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o, st = kda.kda_fwd_chunked_fused(q, k, v, g, b, s0, gate_scale=c, chunk=64)
+    torch.cuda.synchronize()
+    o, st = to_np(o), to_np(st)
+    for bb, hh in ((0, 0), (3, 9)):
+        sl = lambda a: np.ascontiguousarray(a[bb:bb + 1, :, hh:hh + 1])
+        o_ref, s_ref = oracle.kda_forward_fused(sl(x["q_raw"]), sl(x["k_raw"]), sl(x["v"]), sl(x["g_raw"]),
+                                                sl(x["b_raw"]), np.ascontiguousarray(x["S0"][bb:bb + 1, hh:hh + 1]),
+                                                gate_scale=c)
+        eo = rel_err(o[bb:bb + 1, :, hh:hh + 1], o_ref)
+        es = rel_err(st[bb:bb + 1, hh:hh + 1], s_ref)
+        log(f"  chain ({bb},{hh}): rel_err o {eo:.2e}  S_T {es:.2e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(st))
