@@ -203,3 +203,24 @@ def test_prefill_fused_prologue_32_column_blocks():
         log(f"  chain ({bb},{hh}): rel_err o {eo:.2e}  S_T {es:.2e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(st))
+
+
+@pytest.mark.parametrize("gate,rule", [("head", "delta"), ("channel", "linear")])
+def test_variants_32_column_blocks(gate, rule):
+    """The per-head gate and the uncorrected write with enough chains (40) that
+    the state pass takes 32-column value blocks on a 256-CU device; the oracle
+    checks two chains."""
+    B, T, H = 4, 1000, 10
+    log(f"[prefill gate={gate} rule={rule} bf16 dk128 dv128 C64 B{B} T{T} H{H}, oracle on 2 chains]")
+    x = prefill_inputs(B, T, H, 128, 128, dtype="bf16", gate_c=0.05, s0_std=0.01, seed=88)
+    o, st = _prefill(x, "bf16", 64, gate, rule)
+    a = _alpha(x, gate)
+    for bb, hh in ((0, 0), (3, 9)):
+        sl = lambda arr: None if arr is None else np.ascontiguousarray(arr[bb:bb + 1, :, hh:hh + 1])
+        o_ref, s_ref = oracle.kda_forward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(a), sl(x["beta"]),
+                                          np.ascontiguousarray(x["S0"][bb:bb + 1, hh:hh + 1]),
+                                          gate=gate, rule=rule)
+        eo = rel_err(o[bb:bb + 1, :, hh:hh + 1], o_ref)
+        es = rel_err(st[bb:bb + 1, hh:hh + 1], s_ref)
+        log(f"  chain ({bb},{hh}): rel_err o {eo:.2e}  S_T {es:.2e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
