@@ -1112,17 +1112,22 @@ constexpr bool fits() {
   return prep_fits<E, DK, C>() && PassCfg<E, DK, dvb_for(DV), C>::smem_bytes <= kLdsLimit;
 }
 
-int g_num_cus = 0;
+// CU count of the current device, cached per device (relaxed atomics: every
+// thread that fills an entry writes the same value; devices past 63 are
+// queried on every call; 256 if the query fails).
 int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return g_num_cus;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // State pass with value blocks of DVB columns: one workgroup per (chain,

@@ -14,8 +14,10 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates or frees device memory and keeps no global
- *     mutable state.
+ *     library never allocates or frees device memory and keeps no state
+ *     between calls beyond two process-wide caches: the device's CU count
+ *     (read once) and, per kernel, whether it has already opted in to more
+ *     than 64 KiB of LDS on a device (set once, thread-safely).
  *   - Tensors are contiguous and row-major.  Pointers must be 16-byte aligned.
  *   - `dtype` selects the element type of q, k, v, alpha, beta and o:
  *     KDA_F32 (IEEE fp32) or KDA_BF16 (bfloat16).  The state is always fp32.
