@@ -33,7 +33,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PREFILL = "prefill_b4_h16_t16k"
 LONG = "prefill_h16_t128k"
 DECODE = "decode_b256_h16"
-DECODE_POOL = 16
 
 
 def prefill_alg_bytes(B, T, H, dk, dv, elem=2, gate_per_channel=True) -> int:
@@ -147,26 +146,38 @@ def bench_prefill(name: str, steps: int, warmup: int, gate: str = "channel"):
 
 
 def bench_decode(steps: int, warmup: int):
+    """warmup + steps consecutive decode steps, each with its own inputs (drawn
+    on the host in blocks and uploaded once before timing), on the carried
+    fp32 state."""
     import torch
     import gated_delta_rule_76_amd as kda
-    from synth import WORKLOADS, decode_pool
+    from synth import WORKLOADS, decode_state, decode_steps
 
     w = WORKLOADS[DECODE]
-    p = decode_pool(w.B, w.H, w.d_k, w.d_v, pool=DECODE_POOL, dtype=w.dtype, gate_c=w.gate_c,
-                    s0_std=w.s0_std, seed=w.seed)
-    d = _upload(p, ("q", "k", "v", "alpha", "beta"), w.dtype)
-    S = torch.from_numpy(p["S"]).cuda()
+    n = warmup + steps
+    S = torch.from_numpy(decode_state(w.B, w.H, w.d_k, w.d_v, s0_std=w.s0_std, seed=w.seed)).cuda()
+    names = ("q", "k", "v", "alpha", "beta")
+    dims = {"q": (w.d_k,), "k": (w.d_k,), "v": (w.d_v,), "alpha": (w.d_k,), "beta": ()}
+    d = {nm: torch.empty((n, w.B, w.H) + dims[nm], dtype=torch.bfloat16, device="cuda")
+         for nm in names}
+    blk = 100
+    for first in range(0, n, blk):
+        cnt = min(blk, n - first)
+        p = decode_steps(w.B, w.H, w.d_k, w.d_v, first, cnt, dtype=w.dtype, gate_c=w.gate_c,
+                         seed=w.seed)
+        for nm in names:
+            d[nm][first:first + cnt].copy_(torch.from_numpy(p[nm]).to(torch.bfloat16))
+        del p
     o = torch.empty((w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda")
     # Pointers are resolved once so the timed loop is the C entry point alone.
-    ptrs = [tuple(d[n][i].data_ptr() for n in ("q", "k", "v", "alpha", "beta"))
-            for i in range(DECODE_POOL)]
+    ptrs = [tuple(d[nm][i].data_ptr() for nm in names) for i in range(n)]
     sp, op = S.data_ptr(), o.data_ptr()
     stream = torch.cuda.current_stream().cuda_stream
     call = kda.lib().kda_decode_step
     step = [0]
 
     def fn():
-        i = step[0] % DECODE_POOL
+        i = step[0]
         step[0] += 1
         st = call(*ptrs[i], sp, op, w.B, w.H, w.d_k, w.d_v, kda.KDA_BF16, stream)
         if st != 0:

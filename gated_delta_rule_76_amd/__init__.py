@@ -20,7 +20,8 @@ __all__ = [
     "KDA_F32", "KDA_BF16", "GATES", "RULES", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
     "kda_fwd_chunked_fused", "kda_decode_step_fused", "attnres_forward", "attnres_forward_raw",
-    "status_string", "version", "workspace_bytes",
+    "status_string", "version", "workspace_bytes", "set_wait_limit", "wait_limit",
+    "set_ring_cap", "ring_cap",
 ]
 
 KDA_F32 = 0
@@ -33,7 +34,9 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
 # Every symbol include/kda.h declares.
 ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
                "kda_fwd_chunked_fused", "kda_fwd_chunked_workspace_bytes", "kda_decode_step",
-               "kda_decode_step_ex", "kda_decode_step_fused", "attnres_forward")
+               "kda_decode_step_ex", "kda_decode_step_fused", "attnres_forward",
+               "kda_testing_set_wait_limit", "kda_testing_wait_limit",
+               "kda_testing_set_ring_cap", "kda_testing_ring_cap")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -83,6 +86,14 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_step_fused.restype = i
         L.attnres_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         L.attnres_forward.restype = i
+        L.kda_testing_set_wait_limit.argtypes = [i]
+        L.kda_testing_set_wait_limit.restype = i
+        L.kda_testing_wait_limit.argtypes = []
+        L.kda_testing_wait_limit.restype = i
+        L.kda_testing_set_ring_cap.argtypes = [sz]
+        L.kda_testing_set_ring_cap.restype = i
+        L.kda_testing_ring_cap.argtypes = []
+        L.kda_testing_ring_cap.restype = sz
         _lib = L
     return _lib
 
@@ -94,6 +105,26 @@ def exported_symbols() -> Tuple[str, ...]:
 
 def version() -> int:
     return int(lib().kda_version())
+
+
+def set_wait_limit(polls: int) -> int:
+    """Test hook (include/kda_testing.h): polls before a prefill output wave
+    gives up on a chunk's hand-over and writes NaN for it.  Returns the status."""
+    return int(lib().kda_testing_set_wait_limit(int(polls)))
+
+
+def wait_limit() -> int:
+    return int(lib().kda_testing_wait_limit())
+
+
+def set_ring_cap(nbytes: int) -> int:
+    """Test hook (include/kda_testing.h): slot budget of the prefill's segment
+    ring in bytes (0 restores the default).  Returns the status."""
+    return int(lib().kda_testing_set_ring_cap(int(nbytes)))
+
+
+def ring_cap() -> int:
+    return int(lib().kda_testing_ring_cap())
 
 
 def status_string(status: int) -> str:

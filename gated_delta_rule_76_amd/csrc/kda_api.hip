@@ -2,8 +2,23 @@
 // The contract (layouts, ownership, errors) is documented in include/kda.h.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kda.h"
+#include "../../include/kda_testing.h"
 #include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+std::atomic<int> g_wait_limit{1 << 24};
+std::atomic<size_t> g_ring_cap{kRingCap};
+}  // namespace
+
+int wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+size_t ring_cap() { return g_ring_cap.load(std::memory_order_relaxed); }
+
+}  // namespace kda
 
 namespace {
 
@@ -28,6 +43,21 @@ extern "C" {
 
 int kda_version(void) { return kVersion; }
 
+int kda_testing_set_wait_limit(int polls) {
+  if (polls < 0) return KDA_ERR_INVALID_ARG;
+  kda::g_wait_limit.store(polls, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+int kda_testing_wait_limit(void) { return kda::wait_limit(); }
+
+int kda_testing_set_ring_cap(size_t bytes) {
+  kda::g_ring_cap.store(bytes == 0 ? kda::kRingCap : bytes, std::memory_order_relaxed);
+  return KDA_OK;
+}
+
+size_t kda_testing_ring_cap(void) { return kda::ring_cap(); }
+
 const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";
@@ -44,8 +74,11 @@ size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v, in
   if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
   size_t slot = 0;
   if (!kda::prefill_slot_bytes(dtype == KDA_BF16, d_k, d_v, chunk, &slot)) return 0;
-  const size_t nchunk = (static_cast<size_t>(T) + chunk - 1) / chunk;
-  return static_cast<size_t>(B) * H * nchunk * slot;
+  const long long nchunk = (static_cast<long long>(T) + chunk - 1) / chunk;
+  if (static_cast<long long>(B) * H * nchunk > (1LL << 31) - 1) return 0;
+  return kda::prefill_plan(slot, static_cast<long>(B) * H, static_cast<int>(nchunk), d_k, d_v,
+                           kda::ring_cap())
+      .total;
 }
 
 }  // extern "C"
@@ -81,7 +114,13 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, con
     if (!kda::prefill_supported(dtype == KDA_BF16, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
     const long long nchunk = (static_cast<long long>(T) + chunk - 1) / chunk;
     if (static_cast<long long>(B) * H * nchunk > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
-    const size_t need = kda_fwd_chunked_workspace_bytes(B, T, H, d_k, d_v, chunk, dtype);
+    // one reading of the ring budget for both the size check and the launch
+    const size_t cap = kda::ring_cap();
+    size_t slot = 0;
+    kda::prefill_slot_bytes(dtype == KDA_BF16, d_k, d_v, chunk, &slot);
+    const size_t need =
+        kda::prefill_plan(slot, static_cast<long>(B) * H, static_cast<int>(nchunk), d_k, d_v, cap)
+            .total;
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
       return KDA_ERR_WORKSPACE;
     if (T == 0 && S_T == nullptr) return KDA_OK;
@@ -94,6 +133,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, con
     a.fused = fused; a.gate_scale = gate_scale;
     a.bf16 = dtype == KDA_BF16;
     a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    a.ring_cap = cap;
     a.stream = static_cast<hipStream_t>(stream);
     return from_hip(kda::launch_prefill(a));
   } catch (...) {

@@ -1,6 +1,8 @@
 // Host-side interface between the C ABI (kda_api.hip) and the kernel files.
 #pragma once
 
+#include <stddef.h>
+
 #include <hip/hip_runtime.h>
 
 namespace kda {
@@ -31,9 +33,62 @@ struct PrefillArgs {
   bool fused;        // inputs are raw projections: normalise q, k; map the gate and beta
   float gate_scale;  // alpha = exp(-gate_scale * softplus(g)) when fused
   bool bf16;
-  void* workspace;  // kda_fwd_chunked_workspace_bytes() bytes of device memory
+  void* workspace;         // at least prefill_plan(...).total bytes of device memory
+  size_t workspace_bytes;
+  size_t ring_cap;         // segment ring budget the plan was made with
   hipStream_t stream;
 };
+
+// How a prefill call walks the sequence.  The prep kernel writes one
+// operand slot per (chain, chunk) and the state pass reads it back; when all
+// slots would take more than `ring_cap` bytes, the chunks are cut into
+// segments of `seg` chunks that run one after the other through two ring
+// buffers of `half` bytes each, the state passing from one segment to the
+// next through S_T or, without S_T, through a carrier area of
+// nchain * d_k * d_v fp32 at carrier_off.  The workspace then no longer grows
+// with the sequence length.
+struct PrefillPlan {
+  int seg = 0;             // chunks per segment
+  int nseg = 0;            // segments (1 when everything fits)
+  int nbuf = 1;            // ring buffers in use (2 when segmented)
+  size_t half = 0;         // bytes of one segment's slots (256-byte aligned)
+  size_t carrier_off = 0;  // byte offset of the carrier area (segmented only)
+  size_t total = 0;        // workspace bytes the call needs
+};
+
+constexpr size_t kRingCap = size_t(512) << 20;  // slot budget of kda_fwd_chunked
+
+inline PrefillPlan prefill_plan(size_t slot, long nchain, int nchunk, int d_k, int d_v,
+                                size_t cap) {
+  PrefillPlan p;
+  const size_t full = slot * static_cast<size_t>(nchain) * static_cast<size_t>(nchunk);
+  if (full <= cap || nchunk <= 1) {
+    p.seg = nchunk;
+    p.nseg = 1;
+    p.half = full;
+    p.total = full;
+    return p;
+  }
+  const size_t per_chunk = slot * static_cast<size_t>(nchain);
+  size_t lmax = cap / (2 * per_chunk);
+  if (lmax < 1) lmax = 1;
+  p.nseg = static_cast<int>((static_cast<size_t>(nchunk) + lmax - 1) / lmax);
+  p.seg = (nchunk + p.nseg - 1) / p.nseg;
+  p.nbuf = 2;
+  p.half = (per_chunk * static_cast<size_t>(p.seg) + 255) / 256 * 256;
+  p.carrier_off = 2 * p.half;
+  p.total = p.carrier_off + static_cast<size_t>(nchain) * d_k * d_v * sizeof(float);
+  return p;
+}
+
+// Polls an output wave of the prefill state pass makes while it waits for
+// the state wave's U of a chunk before it gives up and writes NaN for that
+// chunk (default 1 << 24; kda_testing_set_wait_limit changes it).
+int wait_limit();
+
+// Slot budget of kda_fwd_chunked's segment ring (kRingCap unless a test
+// changed it with kda_testing_set_ring_cap).
+size_t ring_cap();
 
 // Launch one decode step (validated arguments).
 hipError_t launch_decode(const DecodeArgs& a);

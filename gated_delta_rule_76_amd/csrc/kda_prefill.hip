@@ -303,8 +303,8 @@ template <typename E, int DK, int C, bool CHANNEL>
 __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     const typename E::storage* __restrict__ q, const typename E::storage* __restrict__ k,
     const typename E::storage* __restrict__ alpha, const typename E::storage* __restrict__ beta,
-    char* __restrict__ ws, int T, int H, int nchunk, int ntask, int gate, int rule, int fused,
-    float gscale) {
+    char* __restrict__ ws, int T, int H, int n0, int nchunk, int ntask, int gate, int rule,
+    int fused, float gscale) {
   using S = Shape<E, DK, C>;
   using P = PrepCfg<E, DK, C>;
   using M = typename S::M;
@@ -328,12 +328,13 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   const int ch0 = 8 * cg;
 
   // Token row of (task, r), clamped into the sequence so loads stay in bounds.
-  // Tasks are chunk-major (task = n * nchain + chain), so the workspace holds
-  // chunk n of every chain in one contiguous run, which the state pass reads
-  // at its step n.
+  // This launch covers chunks n0 .. n0 + nchunk - 1 of every chain.  Tasks
+  // are chunk-major (task = (n - n0) * nchain + chain), so the workspace
+  // holds chunk n of every chain in one contiguous run, which the state pass
+  // reads at its step n.
   const int nchain = ntask / nchunk;
   auto rowptr = [&](int task, int r) -> long {
-    const int n = task / nchain, chain = task - n * nchain;
+    const int nl = task / nchain, chain = task - nl * nchain, n = n0 + nl;
     const int b = chain / H, h = chain - b * H;
     const int t = min(n * C + r, T - 1);
     return (static_cast<long>(b) * T + t) * H + h;
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   };
 
   for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int n = task / nchain;
+    const int n = n0 + task / nchain;
     const int valid = min(C, T - n * C);
     char* slot = ws + static_cast<long>(task) * S::SLOT;
 
@@ -730,7 +731,12 @@ struct PassCfg {
   static constexpr size_t smem_bytes = static_cast<size_t>(OFF_FLAG) + 64;
 };
 
-// One workgroup per (batch, head, block of DVB value columns).  Each
+// One workgroup per (batch, head, block of DVB value columns), over chunks
+// n0 .. n0 + nchunk - 1 of the sequence (a segment; the whole sequence when
+// it fits the workspace).  Inside the kernel n counts chunks from n0: slot n
+// of the workspace, buffer parities and the hand-over counters all use it;
+// token rows are (n0 + n) * C + r.  S0 is the state entering chunk n0 (NULL:
+// zero), ST receives the state after the last chunk (NULL: not stored).  Each
 // 16-column slab of the fp32 state has a state wave, which keeps the slab in
 // accumulator registers and runs the sequential chain, and an output wave on
 // another SIMD, which forms the slab's output from the state and U the state
@@ -752,7 +758,7 @@ __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH))
 __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, DVB, C>::WPE))) void state_pass_kernel(
     const char* __restrict__ ws, const typename E::storage* __restrict__ v,
     const float* __restrict__ S0, typename E::storage* __restrict__ o, float* __restrict__ ST,
-    int T, int H, int DV, int nchunk, int rule) {
+    int T, int H, int DV, int n0, int nchunk, int rule, int wait_limit) {
   using S = Shape<E, DK, C>;
   using K = PassCfg<E, DK, DVB, C>;
   using M = typename S::M;
@@ -780,7 +786,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   auto stage_v = [&](int n) {
     char* dst = lds + K::OFF_V + (n & 1) * K::VTILE;
     for (int u = cw; u < K::NVI; u += K::NCP) {
-      const int t = min(n * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
+      const int t = min((n0 + n) * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
       const char* src = reinterpret_cast<const char*>(v + base + t * rs) + cbyte;
       __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
     }
@@ -799,7 +805,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)sink, 16, 0, 0);
     }
     for (int u = 0; u < K::NVI; ++u) {
-      const int t = min(n * C + u * K::RPI + crow, T - 1);
+      const int t = min((n0 + n) * C + u * K::RPI + crow, T - 1);
       __builtin_amdgcn_global_load_lds((gvoid_t*)(reinterpret_cast<const char*>(v + base + t * rs) + cbyte), (lvoid_t*)sink, 16, 0, 0);
     }
   };
@@ -820,7 +826,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     }
 #pragma unroll
     for (int u = 0; u < K::NVI; ++u) {
-      const int r = u * K::RPI + crow, t = n * C + r;
+      const int r = u * K::RPI + crow, t = (n0 + n) * C + r;
       if (r < C && t < T) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x[u];
     }
   };
@@ -873,7 +879,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
                           S::NTK == 8 && S::NTK * S::NCS == 16 && S::FRAG == 1024;
     auto chain_step = [&](int n, auto delta_rule) {
       constexpr bool DELTA = decltype(delta_rule)::value;
-      const int t0 = n * C;
+      const int t0 = (n0 + n) * C;
       const char* sl = slot_of(n);
       auto fr = [&](int off, int idx) -> frag {
         return reinterpret_cast<const frag*>(sl + off + idx * S::FRAG)[lane];
@@ -1032,9 +1038,15 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
       for (int i = 0; i < S::NTRI; ++i) app[i] = fr(S::OFF_PP, i);
       // U of this chunk: the state wave publishes it part-way through the
-      // chunk.  The wait is bounded; the state wave never waits on this wave.
-      for (int it = 0; it < (1 << 24); ++it) {
-        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > n) break;
+      // chunk.  The wait is bounded (wait_limit polls; the state wave never
+      // waits on this wave).  If it gives up, the chunk's output is NaN, so
+      // the failure shows in the result instead of a stale U.
+      bool ready = false;
+      for (int it = 0; it < wait_limit; ++it) {
+        if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > n) {
+          ready = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
       frag ufr[S::NCS];
@@ -1044,6 +1056,10 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
       for (int s2 = 0; s2 < S::NCS; ++s2)
 #pragma unroll
         for (int tr = 2 * s2; tr < S::NT; ++tr) O[tr] = M::mma(app[S::tri(tr) + s2], ufr[s2], O[tr]);
+      if (!ready) {
+#pragma unroll
+        for (int tr = 0; tr < S::NT; ++tr) O[tr] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      }
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
@@ -1131,9 +1147,10 @@ int num_cus() {
 }
 
 // State pass with value blocks of DVB columns: one workgroup per (chain,
-// value block).
+// value block), over chunks n0 .. n0 + cnt - 1.
 template <typename E, int DK, int DVB, int C>
-hipError_t launch_pass(const PrefillArgs& a, const char* ws, int nchunk) {
+hipError_t launch_pass(const PrefillArgs& a, const char* ws, int n0, int cnt, const float* s_in,
+                       float* s_out) {
   using St = typename E::storage;
   using K = PassCfg<E, DK, DVB, C>;
   // Opt in to more than 64 KiB of LDS, once per device (bit d of the mask;
@@ -1155,37 +1172,62 @@ hipError_t launch_pass(const PrefillArgs& a, const char* ws, int nchunk) {
   // one XCD (and its L2) whenever gridDim.x is a multiple of 8.
   hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, a.d_v / DVB),
                      dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
-                     a.S0, static_cast<St*>(a.o), a.S_T, a.T, a.H, a.d_v, nchunk, a.rule);
+                     s_in, static_cast<St*>(a.o), s_out, a.T, a.H, a.d_v, n0, cnt, a.rule,
+                     wait_limit());
+  return hipGetLastError();
+}
+
+template <typename E, int DK, int C>
+hipError_t launch_prep(const PrefillArgs& a, char* ws, int n0, int cnt) {
+  using St = typename E::storage;
+  const long ntask = static_cast<long>(a.B) * a.H * cnt;
+  if (ntask == 0) return hipSuccess;
+  // two resident workgroups per CU, each walking a strided list of chunks
+  const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
+  auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
+  hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
+                     static_cast<const St*>(a.q), static_cast<const St*>(a.k),
+                     static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
+                     a.H, n0, cnt, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
+                     a.gate_scale);
   return hipGetLastError();
 }
 
 template <typename E, int DK, int DV, int C>
 hipError_t launch_t(const PrefillArgs& a) {
-  using St = typename E::storage;
   const int nchunk = (a.T + C - 1) / C;
-  const long ntask = static_cast<long>(a.B) * a.H * nchunk;
+  const PrefillPlan p = prefill_plan(Shape<E, DK, C>::SLOT, static_cast<long>(a.B) * a.H, nchunk,
+                                     DK, DV, a.ring_cap);
+  if (a.workspace_bytes < p.total) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(a.workspace);
-  if (ntask > 0) {
-    // two resident workgroups per CU, each walking a strided list of chunks
-    const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
-    auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
-    hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
-                       static_cast<const St*>(a.q), static_cast<const St*>(a.k),
-                       static_cast<const St*>(a.alpha), static_cast<const St*>(a.beta), ws, a.T,
-                       a.H, nchunk, static_cast<int>(ntask), a.gate, a.rule, a.fused ? 1 : 0,
-                       a.gate_scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // The state passes from segment to segment through S_T when the caller
+  // wants it, else through the workspace's carrier area.
+  float* carrier = a.S_T != nullptr ? a.S_T : reinterpret_cast<float*>(ws + p.carrier_off);
   // The chain of each value block is sequential over the chunks.  When the
   // 32-column blocks would leave more than half of the CUs idle (few long
   // sequences), 16-column blocks put twice as many chains of work on the
   // chip, each CU carrying one state slab instead of two.
-  if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit) {
-    if (static_cast<long>(a.B) * a.H * (DV / 32) * 2 <= num_cus())
-      return launch_pass<E, DK, 16, C>(a, ws, nchunk);
+  bool narrow = false;
+  if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit)
+    narrow = static_cast<long>(a.B) * a.H * (DV / 32) * 2 <= num_cus();
+  for (int i = 0; i < p.nseg; ++i) {
+    const int n0 = i * p.seg, cnt = min(p.seg, nchunk - n0);
+    char* base = ws + static_cast<size_t>(i % p.nbuf) * p.half;
+    hipError_t e = launch_prep<E, DK, C>(a, base, n0, cnt);
+    if (e != hipSuccess) return e;
+    const float* s_in = i == 0 ? a.S0 : carrier;
+    float* s_out = i == p.nseg - 1 ? a.S_T : carrier;
+    if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit) {
+      if (narrow) {
+        e = launch_pass<E, DK, 16, C>(a, base, n0, cnt, s_in, s_out);
+        if (e != hipSuccess) return e;
+        continue;
+      }
+    }
+    e = launch_pass<E, DK, dvb_for(DV), C>(a, base, n0, cnt, s_in, s_out);
+    if (e != hipSuccess) return e;
   }
-  return launch_pass<E, DK, dvb_for(DV), C>(a, ws, nchunk);
+  return hipSuccess;
 }
 
 template <typename E, int DK, int C>

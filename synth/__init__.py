@@ -47,6 +47,8 @@ __all__ = [
     "round_to_bf16",
     "prefill_inputs",
     "decode_pool",
+    "decode_steps",
+    "decode_state",
     "orthonormal_key_set",
 ]
 
@@ -81,13 +83,17 @@ _BLOCK = 1 << 15
 _TENSORS = ("q", "k", "v", "alpha", "beta")
 
 
-def _fill_block(out: dict, tid_seed: int, j: int, d_k: int, d_v: int, gate_c: float,
-                bf16: bool) -> None:
-    lo = j * _BLOCK
-    hi = min(lo + _BLOCK, out["q"].shape[0])
+def _fill_block(out: dict, tid_seed, j: int, d_k: int, d_v: int, gate_c: float,
+                bf16: bool, rows: int = _BLOCK) -> None:
+    """Fill rows [j*rows, (j+1)*rows) of every token tensor.  `tid_seed` is an
+    int or a tuple of ints; block j of tensor i draws from
+    PCG64(SeedSequence([*tid_seed, i, j]))."""
+    lo = j * rows
+    hi = min(lo + rows, out["q"].shape[0])
     n = hi - lo
+    prefix = list(tid_seed) if isinstance(tid_seed, tuple) else [tid_seed]
     for ti, name in enumerate(_TENSORS):
-        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([tid_seed, ti, j])))
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(prefix + [ti, j])))
         if name in ("q", "k"):
             x = rng.standard_normal((n, d_k), dtype=np.float32)
             _l2_normalise_(x)
@@ -208,6 +214,50 @@ def decode_pool(B: int, H: int, d_k: int, d_v: int, *, pool: int, dtype: str = "
     out = _draw_token_tensors(seed, (pool, B, H), d_k, d_v, gate_c, dtype == "bf16")
     out["S"] = _draw_state(seed, (B, H, d_k, d_v), s0_std)
     return out
+
+
+# Entropy tag of per-step decode draws (keeps them apart from prefill draws).
+_DECODE_TAG = 0xDEC0DE
+
+
+def decode_state(B: int, H: int, d_k: int, d_v: int, *, s0_std: float = 0.01,
+                 seed: int = 4) -> np.ndarray:
+    """Initial fp32 state S [B,H,d_k,d_v] = s0_std * N(0,1) of a decode run."""
+    return _draw_state(seed, (B, H, d_k, d_v), s0_std)
+
+
+def decode_steps(B: int, H: int, d_k: int, d_v: int, first: int, count: int, *,
+                 dtype: str = "bf16", gate_c: float = 0.05, seed: int = 4) -> dict:
+    """Inputs of decode steps first .. first+count-1, stacked on a leading step
+    axis: q, k, alpha [count,B,H,d_k]; v [count,B,H,d_v]; beta [count,B,H]
+    (float32, bf16-exact when dtype == "bf16").  Step s draws tensor i from
+    PCG64(SeedSequence([seed, tag, s, i, 0])), so its values depend on (seed, s)
+    alone and a long run can be drawn in pieces; every step is distinct."""
+    import concurrent.futures as cf
+    import os
+
+    rows = B * H
+    out = {"q": np.empty((count * rows, d_k), np.float32),
+           "k": np.empty((count * rows, d_k), np.float32),
+           "v": np.empty((count * rows, d_v), np.float32),
+           "alpha": np.empty((count * rows, d_k), np.float32),
+           "beta": np.empty((count * rows,), np.float32)}
+
+    def one(i):
+        # each step is its own block of B*H rows; views keep step i's rows apart
+        view = {n: a[i * rows:(i + 1) * rows] for n, a in out.items()}
+        _fill_block(view, (seed, _DECODE_TAG, first + i), 0, d_k, d_v, gate_c, dtype == "bf16",
+                    rows=rows)
+
+    workers = max(1, min(count, os.cpu_count() or 1, 16))
+    if workers == 1:
+        for i in range(count):
+            one(i)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(count)))
+    lead = (count, B, H)
+    return {n: a.reshape(lead + a.shape[1:]) for n, a in out.items()}
 
 
 def orthonormal_key_set(d: int, kind: str = "hadamard") -> np.ndarray:

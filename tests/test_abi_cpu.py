@@ -36,12 +36,47 @@ def test_version_and_status_strings():
     assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
 
 
+def test_wait_limit_hook():
+    default = kda.wait_limit()
+    assert default == 1 << 24
+    try:
+        assert kda.set_wait_limit(-1) == 1          # KDA_ERR_INVALID_ARG
+        assert kda.wait_limit() == default
+        assert kda.set_wait_limit(0) == 0 and kda.wait_limit() == 0
+    finally:
+        assert kda.set_wait_limit(default) == 0
+    assert kda.wait_limit() == default
+
+
+def test_ring_cap_hook():
+    ws = kda.lib().kda_fwd_chunked_workspace_bytes
+    one = ws(1, 64, 1, 128, 128, 64, kda.KDA_BF16)
+    assert kda.ring_cap() == 512 << 20
+    try:
+        kda.set_ring_cap(3 * one)           # room for one chunk of one chain per ring buffer
+        assert kda.ring_cap() == 3 * one
+        assert ws(1, 64, 1, 128, 128, 64, kda.KDA_BF16) == one            # one chunk: no ring
+        assert ws(1, 640, 1, 128, 128, 64, kda.KDA_BF16) == 2 * one + 128 * 128 * 4
+        assert ws(2, 640, 1, 128, 128, 64, kda.KDA_BF16) == 4 * one + 2 * 128 * 128 * 4
+    finally:
+        kda.set_ring_cap(0)
+    assert kda.ring_cap() == 512 << 20
+
+
 def test_workspace_query():
     ws = kda.lib().kda_fwd_chunked_workspace_bytes
     one = ws(1, 64, 1, 128, 128, 64, kda.KDA_BF16)      # one chunk's slot
-    assert one % 1024 == 0 and 60 * 1024 <= one <= 66 * 1024
-    assert ws(4, 16384, 16, 128, 128, 64, kda.KDA_BF16) == 4 * 16 * 256 * one
+    assert one % 1024 == 0 and 60 * 1024 <= one <= 62 * 1024
     assert ws(1, 65, 1, 128, 128, 64, kda.KDA_BF16) == 2 * one   # ragged tail: one more slot
+    assert ws(4, 4096, 16, 128, 128, 64, kda.KDA_BF16) == 4 * 16 * 64 * one  # fits: no ring
+    # Past the 512 MiB slot budget the sequence runs in segments through two
+    # ring buffers plus a carrier state: the size stops growing with T.
+    cap, state = 512 << 20, 4 * 16 * 128 * 128 * 4
+    big = ws(4, 16384, 16, 128, 128, 64, kda.KDA_BF16)
+    assert big == 2 * 64 * 64 * one + state                     # 4 segments of 64 chunks
+    assert big <= cap + state
+    assert ws(4, 1 << 20, 16, 128, 128, 64, kda.KDA_BF16) <= cap + state
+    assert ws(1, 1 << 22, 16, 128, 128, 64, kda.KDA_BF16) <= cap + 16 * 128 * 128 * 4
     assert ws(1, 0, 1, 128, 128, 64, kda.KDA_BF16) == 0
     assert ws(1, 64, 1, 128, 128, 64, kda.KDA_F32) == 0          # unsupported combination
     assert ws(1, 64, 1, 48, 128, 64, kda.KDA_BF16) == 0

@@ -313,3 +313,80 @@ def test_fused_prologue_on_unit_inputs_matches_plain_path():
     torch.cuda.synchronize()
     assert rel_err(to_np(o_f), to_np(o_p)) <= TOL["bf16"]
     assert rel_err(to_np(s_f), to_np(s_p)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 32)])
+def test_wait_give_up_is_visible(dtype, C):
+    """With the host's poll bound at zero, every output wave gives up on its
+    chunk's hand-over at once: the output must come back all NaN (the failure
+    is visible) while the state is unaffected, and every kernel exits."""
+    kda = _kda()
+    log(f"[wait give-up] {dtype} dk128 C{C} B2 T150 H3, poll bound 0")
+    x = prefill_inputs(2, 150, 3, 128, 128, dtype=dtype, seed=31)
+    o_ok, s_ok = run_prefill(x, dtype, C)
+    default = kda.wait_limit()
+    try:
+        assert kda.set_wait_limit(0) == 0
+        o_bad, s_bad = run_prefill(x, dtype, C)
+    finally:
+        assert kda.set_wait_limit(default) == 0
+    assert np.all(np.isnan(o_bad))
+    np.testing.assert_array_equal(s_bad, s_ok)
+    o_again, _ = run_prefill(x, dtype, C)
+    np.testing.assert_array_equal(o_again, o_ok)
+
+
+def _run_capped(x, dtype, C, cap, *, S0=True, want_state=True, alias=False):
+    """kda_fwd_chunked with the segment-ring budget set to `cap` bytes (0 =
+    default); returns (o, S_T or None) as fp64 numpy."""
+    import torch
+    kda = _kda()
+    q, k, v, a, b = _dev_inputs(x, dtype)
+    s0 = torch.from_numpy(x["S0"]).cuda() if (S0 and x.get("S0") is not None) else None
+    try:
+        assert kda.set_ring_cap(cap) == 0
+        if alias:
+            o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, S_T=s0)
+        else:
+            o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, return_state=want_state)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_ring_cap(0)
+    return to_np(o), (None if st is None else to_np(st))
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C,B,T,H,segs", [
+    ("bf16", 128, 128, 64, 1, 700, 2, 1),     # one chunk per segment, ragged tail
+    ("bf16", 128, 128, 64, 2, 1000, 3, 3),    # three chunks per segment
+    ("bf16", 128, 128, 64, 4, 520, 10, 2),    # 32-column value blocks
+    ("bf16", 64, 32, 32, 3, 333, 2, 4),
+    ("f32", 128, 128, 32, 1, 200, 2, 2),
+    ("f32", 16, 16, 16, 2, 77, 1, 1),
+])
+def test_segmented_prefill_is_bitwise_the_single_pass(dtype, dk, dv, C, B, T, H, segs):
+    """A ring budget of `segs` chunks (of every chain) per ring buffer runs the
+    sequence in segments that hand the state on through S_T or the carrier
+    area; every segment does the same operations on the same values as one
+    long pass, so the results must match bitwise, and the oracle."""
+    kda = _kda()
+    log(f"[segmented] {dtype} dk{dk} dv{dv} C{C} B{B} T{T} H{H}, {segs} chunk(s) per segment")
+    x = prefill_inputs(B, T, H, dk, dv, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=dk + T + segs)
+    code = kda.KDA_BF16 if dtype == "bf16" else kda.KDA_F32
+    one = kda.workspace_bytes(1, C, 1, dk, dv, C, code)   # one slot
+    cap = 2 * segs * B * H * one
+    o1, s1 = _run_capped(x, dtype, C, 0)
+    o2, s2 = _run_capped(x, dtype, C, cap)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+    o3, s3 = _run_capped(x, dtype, C, cap, want_state=False)     # carrier area in the workspace
+    assert s3 is None
+    np.testing.assert_array_equal(o1, o3)
+    o4, s4 = _run_capped(x, dtype, C, cap, alias=True)           # S_T aliases S0
+    np.testing.assert_array_equal(o1, o4)
+    np.testing.assert_array_equal(s1, s4)
+    o5, s5 = _run_capped(x, dtype, C, cap, S0=False)             # zero initial state
+    o6, s6 = _run_capped(x, dtype, C, 0, S0=False)
+    np.testing.assert_array_equal(o5, o6)
+    np.testing.assert_array_equal(s5, s6)
+    o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    assert rel_err(o2, o_ref) <= TOL[dtype] and rel_err(s2, s_ref) <= TOL[dtype]

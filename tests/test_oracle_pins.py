@@ -433,3 +433,43 @@ def test_prologue_feeds_the_recurrence():
     q, k, a, b = oracle.input_prologue(x["q_raw"], x["k_raw"], x["g_raw"], x["b_raw"], 0.2)
     o2, s2 = oracle.kda_forward(q, k, x["v"], a, b, x["S0"])
     assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+@pytest.mark.parametrize("rule", ["delta", "linear"])
+def test_fused_variants_dense_page_form(gate, rule):
+    """The fused oracle for every gate and rule against a loop written from the
+    pages with dense matrices, fed by maps computed here from their own
+    definitions: unit q and k (section 3's projection reading), alpha =
+    exp(-c log(1 + e^g)) as a gate in [0, 1] (section 4), beta the logistic
+    function.  The loop applies S_t = A_t S_{t-1} + B_t with A_t =
+    (I - beta_t k_t k_t^T) Diag(alpha_t) for the delta rule (section 4) or
+    Diag(alpha_t) without the erase (section 2.1's write with the gate), B_t =
+    beta_t k_t v_t^T, then reads o_t = S_t^T q_t (section 2.1)."""
+    rng = np.random.default_rng(61)
+    B, T, H, dk, dv, c = 2, 7, 3, 6, 4, 0.7
+    q_raw = rng.standard_normal((B, T, H, dk)) * 3.0
+    k_raw = rng.standard_normal((B, T, H, dk))
+    v = rng.standard_normal((B, T, H, dv))
+    g_raw = rng.standard_normal((B, T, H, dk) if gate == "channel" else (B, T, H)) * 2.0
+    b_raw = rng.standard_normal((B, T, H)) * 2.0
+    S0 = 0.2 * rng.standard_normal((B, H, dk, dv))
+    o, ST = oracle.kda_forward_fused(q_raw, k_raw, v, None if gate == "none" else g_raw, b_raw, S0,
+                                     gate_scale=c, gate=gate, rule=rule)
+    for b in range(B):
+        for h in range(H):
+            S = S0[b, h].copy()
+            for t in range(T):
+                qv = q_raw[b, t, h] / np.sqrt(q_raw[b, t, h] @ q_raw[b, t, h])
+                kv = k_raw[b, t, h] / np.sqrt(k_raw[b, t, h] @ k_raw[b, t, h])
+                if gate == "none":
+                    a = np.ones(dk)
+                else:
+                    a = np.broadcast_to(np.exp(-c * np.log1p(np.exp(g_raw[b, t, h]))), (dk,))
+                bt = 1.0 / (1.0 + np.exp(-b_raw[b, t, h]))
+                A = np.diag(a)
+                if rule == "delta":
+                    A = (np.eye(dk) - bt * np.outer(kv, kv)) @ A
+                S = A @ S + bt * np.outer(kv, v[b, t, h])
+                np.testing.assert_allclose(o[b, t, h], S.T @ qv, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(ST[b, h], S, rtol=0, atol=1e-12)

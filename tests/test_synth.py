@@ -40,6 +40,20 @@ def test_decode_pool_shapes():
     assert p["beta"].shape == (3, 4, 2) and p["S"].shape == (4, 2, 16, 8)
 
 
+def test_decode_steps_are_distinct_and_drawn_piecewise():
+    from synth import decode_state, decode_steps
+    whole = decode_steps(3, 2, 16, 8, 0, 6, dtype="bf16")
+    part = decode_steps(3, 2, 16, 8, 4, 2, dtype="bf16")
+    for n in whole:
+        np.testing.assert_array_equal(whole[n][4:], part[n])
+        assert not np.array_equal(whole[n][0], whole[n][1])
+        np.testing.assert_array_equal(round_to_bf16(whole[n]), whole[n])
+    assert whole["alpha"].shape == (6, 3, 2, 16) and whole["beta"].shape == (6, 3, 2)
+    assert np.all((whole["alpha"] > 0) & (whole["alpha"] <= 1))
+    s = decode_state(3, 2, 16, 8)
+    assert s.shape == (3, 2, 16, 8) and s.dtype == np.float32
+
+
 def test_orthonormal_keys_exact():
     for d, kind in [(16, "hadamard"), (64, "hadamard"), (32, "onehot"), (8, "signed")]:
         K = orthonormal_key_set(d, kind).astype(np.float64)
