@@ -19,6 +19,7 @@ from typing import Optional, Tuple
 __all__ = [
     "KDA_F32", "KDA_BF16", "GATES", "RULES", "KdaError", "lib", "library_path", "exported_symbols",
     "kda_fwd_chunked", "kda_decode_step", "kda_fwd_chunked_raw", "kda_decode_step_raw",
+    "kda_fwd_chunked_noalloc_raw",
     "kda_fwd_chunked_fused", "kda_decode_step_fused", "attnres_forward", "attnres_forward_raw",
     "status_string", "version", "workspace_bytes", "set_wait_limit", "wait_limit",
     "set_ring_cap", "ring_cap",
@@ -35,6 +36,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
 ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
                "kda_fwd_chunked_fused", "kda_fwd_chunked_workspace_bytes", "kda_decode_step",
                "kda_decode_step_ex", "kda_decode_step_fused", "attnres_forward",
+               "kda_fwd_chunked_noalloc",
                "kda_testing_set_wait_limit", "kda_testing_wait_limit",
                "kda_testing_set_ring_cap", "kda_testing_ring_cap")
 
@@ -86,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_step_fused.restype = i
         L.attnres_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         L.attnres_forward.restype = i
+        L.kda_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                              i, i, vp]
+        L.kda_fwd_chunked_noalloc.restype = i
         L.kda_testing_set_wait_limit.argtypes = [i]
         L.kda_testing_set_wait_limit.restype = i
         L.kda_testing_wait_limit.argtypes = []
@@ -138,6 +143,14 @@ def kda_fwd_chunked_raw(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chu
     return int(lib().kda_fwd_chunked_ex(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v,
                                         chunk, dtype, gate, rule, workspace, workspace_bytes,
                                         stream))
+
+
+def kda_fwd_chunked_noalloc_raw(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk,
+                                dtype, gate=0, rule=0, stream=None) -> int:
+    """kda_fwd_chunked_noalloc with integer pointers: no workspace argument,
+    the library's own device array holds the operand slots."""
+    return int(lib().kda_fwd_chunked_noalloc(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v,
+                                             chunk, dtype, gate, rule, stream))
 
 
 def kda_decode_step_raw(q, k, v, alpha, beta, S, o, B, H, d_k, d_v, dtype, stream=None,

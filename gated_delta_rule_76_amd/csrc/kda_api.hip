@@ -88,7 +88,7 @@ namespace {
 int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, const void* beta,
              const float* S0, void* o, float* S_T, int B, int T, int H, int d_k, int d_v,
              int chunk, int dtype, int gate, int rule, bool fused, float gate_scale,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
   try {
     if (B < 1 || H < 1 || T < 0 || !dtype_ok(dtype) || !gate_ok(gate) || !rule_ok(rule) ||
         !scale_ok(gate_scale))
@@ -114,15 +114,23 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, con
     if (!kda::prefill_supported(dtype == KDA_BF16, d_k, d_v, chunk)) return KDA_ERR_UNSUPPORTED;
     const long long nchunk = (static_cast<long long>(T) + chunk - 1) / chunk;
     if (static_cast<long long>(B) * H * nchunk > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
-    // one reading of the ring budget for both the size check and the launch
-    const size_t cap = kda::ring_cap();
     size_t slot = 0;
     kda::prefill_slot_bytes(dtype == KDA_BF16, d_k, d_v, chunk, &slot);
-    const size_t need =
-        kda::prefill_plan(slot, static_cast<long>(B) * H, static_cast<int>(nchunk), d_k, d_v, cap)
-            .total;
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
-      return KDA_ERR_WORKSPACE;
+    size_t cap = 0;
+    if (noalloc) {
+      // the library's own device array must hold the whole plan
+      if (!kda::noalloc_plan(slot, static_cast<long>(B) * H, static_cast<int>(nchunk), d_k, d_v,
+                             &cap))
+        return KDA_ERR_WORKSPACE;
+    } else {
+      // one reading of the ring budget for both the size check and the launch
+      cap = kda::ring_cap();
+      const size_t need = kda::prefill_plan(slot, static_cast<long>(B) * H,
+                                            static_cast<int>(nchunk), d_k, d_v, cap)
+                              .total;
+      if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return KDA_ERR_WORKSPACE;
+    }
     if (T == 0 && S_T == nullptr) return KDA_OK;
 
     kda::PrefillArgs a;
@@ -136,7 +144,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, con
     a.workspace_bytes = workspace_bytes;
     a.ring_cap = cap;
     a.stream = static_cast<hipStream_t>(stream);
-    return from_hip(kda::launch_prefill(a));
+    return from_hip(noalloc ? kda::launch_prefill_noalloc(a) : kda::launch_prefill(a));
   } catch (...) {
     return KDA_ERR_HIP;
   }
@@ -185,6 +193,14 @@ int kda_fwd_chunked_ex(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype, gate, rule,
                   false, 0.f, workspace, workspace_bytes, stream);
+}
+
+int kda_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                            const void* beta, const float* S0, void* o, float* S_T, int B, int T,
+                            int H, int d_k, int d_v, int chunk, int dtype, int gate, int rule,
+                            void* stream) {
+  return fwd_impl(q, k, v, alpha, beta, S0, o, S_T, B, T, H, d_k, d_v, chunk, dtype, gate, rule,
+                  false, 0.f, nullptr, 0, stream, true);
 }
 
 int kda_fwd_chunked(const void* q, const void* k, const void* v, const void* alpha,

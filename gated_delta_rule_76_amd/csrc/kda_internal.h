@@ -86,6 +86,18 @@ inline PrefillPlan prefill_plan(size_t slot, long nchain, int nchunk, int d_k, i
 // chunk (default 1 << 24; kda_testing_set_wait_limit changes it).
 int wait_limit();
 
+// Size of the device array behind kda_fwd_chunked_noalloc (per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+// Ring budget for an allocation-free prefill of these sizes, such that the
+// whole plan fits kNoAllocScratchBytes; false when no plan fits (too many
+// (batch, head) chains for one chunk of each per ring buffer).
+bool noalloc_plan(size_t slot, long nchain, int nchunk, int d_k, int d_v, size_t* cap);
+
+// Launch the chunked prefill in the library's own device array (validated
+// arguments; a.ring_cap from noalloc_plan).  Allocates nothing.
+hipError_t launch_prefill_noalloc(const PrefillArgs& a);
+
 // Slot budget of kda_fwd_chunked's segment ring (kRingCap unless a test
 // changed it with kda_testing_set_ring_cap).
 size_t ring_cap();

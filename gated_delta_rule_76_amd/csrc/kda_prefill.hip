@@ -54,6 +54,7 @@
 // The reduction does not depend on which k each (lane, element) slot
 // carries as long as both operands agree.
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1272,6 +1273,68 @@ hipError_t dispatch_dk(const PrefillArgs& a, size_t* slot) {
 }
 
 }  // namespace
+
+// --------------------------------------------- prefill without allocation
+// Device memory of the allocation-free prefill: the segment ring (and the
+// carrier state) live in this file-scope array, one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel:
+// it is a host-side stand-in, not a device address.  The address of each
+// device's copy comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Per-device address of `scratch` (devices 0..63 cached; others looked up on
+// every call).  The lookup runs with the device current.
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      cache[dev] = p;
+    }
+    *ptr = cache[dev];
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  *ptr = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool noalloc_plan(size_t slot, long nchain, int nchunk, int d_k, int d_v, size_t* cap) {
+  const size_t full = slot * static_cast<size_t>(nchain) * static_cast<size_t>(nchunk);
+  if (full <= kNoAllocScratchBytes) {  // one segment, no carrier
+    *cap = kNoAllocScratchBytes;
+    return true;
+  }
+  const size_t carrier = static_cast<size_t>(nchain) * d_k * d_v * sizeof(float);
+  if (carrier >= kNoAllocScratchBytes) return false;
+  *cap = kNoAllocScratchBytes - carrier;
+  return prefill_plan(slot, nchain, nchunk, d_k, d_v, *cap).total <= kNoAllocScratchBytes;
+}
+
+hipError_t launch_prefill_noalloc(const PrefillArgs& args) {
+  PrefillArgs a = args;
+  void* p = nullptr;
+  hipError_t e = scratch_address(&p);
+  if (e != hipSuccess) return e;
+  a.workspace = p;
+  a.workspace_bytes = kNoAllocScratchBytes;
+  return launch_prefill(a);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a) {
   return a.bf16 ? dispatch_dk<Bf16>(a, nullptr) : dispatch_dk<F32>(a, nullptr);

@@ -106,12 +106,12 @@ KDA_API const char *kda_status_string(int status);
  *   chunk       : one of 16, 32, 64 (KDA_F32 with d_k = 128 supports chunk
  *                 <= 32: its fp32 chunk tiles would not fit in LDS)
  *   workspace   : device memory of at least kda_fwd_chunked_workspace_bytes()
- *                 bytes, 16-byte aligned, owned by the caller.  It holds one
- *                 slot of per-chunk operand tiles for every chunk of every
- *                 (batch, head) between the two kernels of the call.  Its
- *                 contents on entry are ignored and undefined on return;
- *                 calls that share a workspace must not overlap in time.
- *                 NULL or too small -> KDA_ERR_WORKSPACE.
+ *                 bytes, 16-byte aligned, owned by the caller.  It holds the
+ *                 per-chunk operand tiles between the two kernels of the call
+ *                 (a ring of segments for long sequences, see the size query
+ *                 below).  Its contents on entry are ignored and undefined on
+ *                 return; calls that share a workspace must not overlap in
+ *                 time.  NULL or too small -> KDA_ERR_WORKSPACE.
  *
  * Semantics: T = 0 copies S0 (or zeros) to S_T and leaves o untouched.  A
  * last chunk shorter than `chunk` is handled exactly (padding tokens write
@@ -165,10 +165,36 @@ KDA_API int kda_fwd_chunked_fused(const void *q_raw, const void *k_raw, const vo
                           int d_v, int chunk, int dtype, int gate, int rule, void *workspace,
                           size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace kda_fwd_chunked needs for these sizes:
- * B * H * ceil(T / chunk) * (bytes of one chunk's operand slot, about
- * 65 KiB at d_k = d_v = 128, chunk = 64, bf16).  0 for an unsupported or
- * invalid combination. */
+/*
+ * kda_fwd_chunked_noalloc -- kda_fwd_chunked_ex with no workspace argument,
+ * for callers that cannot allocate device memory (code under stream or graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments
+ * and results are those of kda_fwd_chunked_ex; the operand slots live in a
+ * device array inside the library instead of a caller workspace.
+ *
+ * The array is 64 MiB per GPU (held from the library's load until the
+ * process ends) and is shared by every call on that GPU: calls that overlap
+ * in time on one GPU (on different streams or from different threads) race
+ * and give undefined results.  Nothing in it needs clearing between calls.
+ * The sequence runs in as many segments as the array needs (slower than
+ * kda_fwd_chunked with a full-size workspace for long sequences).  Sizes for
+ * which one chunk of every (batch, head) chain per ring buffer plus the
+ * carried states do not fit the array (B * H above about 350 at d = 128,
+ * chunk = 64, bf16, once the slots of the whole call exceed 64 MiB) return
+ * KDA_ERR_WORKSPACE before anything is launched.  No hipMalloc, hipFree or
+ * allocating library routine is called.
+ */
+KDA_API int kda_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                            const void *alpha, const void *beta, const float *S0, void *o,
+                            float *S_T, int B, int T, int H, int d_k, int d_v, int chunk,
+                            int dtype, int gate, int rule, void *stream);
+
+/* Bytes of workspace kda_fwd_chunked needs for these sizes.  It holds one
+ * operand slot (61 KiB at d_k = d_v = 128, chunk = 64, bf16) per (chain,
+ * chunk) while they fit 512 MiB: B * H * ceil(T / chunk) slots.  Beyond that
+ * the sequence runs in segments through two ring buffers of at least one
+ * chunk of every chain each, plus one carried fp32 state per chain, so the
+ * size stops growing with T.  0 for an unsupported or invalid combination. */
 KDA_API size_t kda_fwd_chunked_workspace_bytes(int B, int T, int H, int d_k, int d_v,
                                        int chunk, int dtype);
 
