@@ -56,6 +56,7 @@
 #include <atomic>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -1184,7 +1185,8 @@ hipError_t launch_prep(const PrefillArgs& a, char* ws, int n0, int cnt) {
   const long ntask = static_cast<long>(a.B) * a.H * cnt;
   if (ntask == 0) return hipSuccess;
   // two resident workgroups per CU, each walking a strided list of chunks
-  const int grid = static_cast<int>(ntask < 2 * num_cus() ? ntask : 2 * num_cus());
+  const int cus = num_cus();
+  const int grid = static_cast<int>(ntask < 2 * cus ? ntask : 2 * cus);
   auto prep = a.gate == kGateChannel ? chunk_prep_kernel<E, DK, C, true> : chunk_prep_kernel<E, DK, C, false>;
   hipLaunchKernelGGL(prep, dim3(grid), dim3(NTH_PREP), 0, a.stream,
                      static_cast<const St*>(a.q), static_cast<const St*>(a.k),
@@ -1211,21 +1213,26 @@ hipError_t launch_t(const PrefillArgs& a) {
   bool narrow = false;
   if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit)
     narrow = static_cast<long>(a.B) * a.H * (DV / 32) * 2 <= num_cus();
-  for (int i = 0; i < p.nseg; ++i) {
-    const int n0 = i * p.seg, cnt = min(p.seg, nchunk - n0);
-    char* base = ws + static_cast<size_t>(i % p.nbuf) * p.half;
-    hipError_t e = launch_prep<E, DK, C>(a, base, n0, cnt);
-    if (e != hipSuccess) return e;
+  auto seg = [&](int i) { return std::make_pair(i * p.seg, min(p.seg, nchunk - i * p.seg)); };
+  auto base = [&](int i) { return ws + static_cast<size_t>(i % p.nbuf) * p.half; };
+  auto pass = [&](int i) -> hipError_t {
+    const auto [n0, cnt] = seg(i);
     const float* s_in = i == 0 ? a.S0 : carrier;
     float* s_out = i == p.nseg - 1 ? a.S_T : carrier;
     if constexpr (dvb_for(DV) == 32 && PassCfg<E, DK, 16, C>::smem_bytes <= kLdsLimit) {
-      if (narrow) {
-        e = launch_pass<E, DK, 16, C>(a, base, n0, cnt, s_in, s_out);
-        if (e != hipSuccess) return e;
-        continue;
-      }
+      if (narrow) return launch_pass<E, DK, 16, C>(a, base(i), n0, cnt, s_in, s_out);
     }
-    e = launch_pass<E, DK, dvb_for(DV), C>(a, base, n0, cnt, s_in, s_out);
+    return launch_pass<E, DK, dvb_for(DV), C>(a, base(i), n0, cnt, s_in, s_out);
+  };
+  auto prep = [&](int i) {
+    const auto [n0, cnt] = seg(i);
+    return launch_prep<E, DK, C>(a, base(i), n0, cnt);
+  };
+
+  for (int i = 0; i < p.nseg; ++i) {
+    hipError_t e = prep(i);
+    if (e != hipSuccess) return e;
+    e = pass(i);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

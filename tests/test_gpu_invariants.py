@@ -336,19 +336,24 @@ def test_wait_give_up_is_visible(dtype, C):
     np.testing.assert_array_equal(o_again, o_ok)
 
 
-def _run_capped(x, dtype, C, cap, *, S0=True, want_state=True, alias=False):
+def _run_capped(x, dtype, C, cap, *, S0=True, want_state=True, alias=False, side=False):
     """kda_fwd_chunked with the segment-ring budget set to `cap` bytes (0 =
-    default); returns (o, S_T or None) as fp64 numpy."""
+    default); returns (o, S_T or None) as fp64 numpy.  side=True calls it on
+    a non-default stream."""
+    import contextlib
     import torch
     kda = _kda()
     q, k, v, a, b = _dev_inputs(x, dtype)
     s0 = torch.from_numpy(x["S0"]).cuda() if (S0 and x.get("S0") is not None) else None
+    torch.cuda.synchronize()
+    ctx = torch.cuda.stream(torch.cuda.Stream()) if side else contextlib.nullcontext()
     try:
         assert kda.set_ring_cap(cap) == 0
-        if alias:
-            o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, S_T=s0)
-        else:
-            o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, return_state=want_state)
+        with ctx:
+            if alias:
+                o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, S_T=s0)
+            else:
+                o, st = kda.kda_fwd_chunked(q, k, v, a, b, s0, chunk=C, return_state=want_state)
         torch.cuda.synchronize()
     finally:
         kda.set_ring_cap(0)
@@ -388,5 +393,11 @@ def test_segmented_prefill_is_bitwise_the_single_pass(dtype, dk, dv, C, B, T, H,
     o6, s6 = _run_capped(x, dtype, C, 0, S0=False)
     np.testing.assert_array_equal(o5, o6)
     np.testing.assert_array_equal(s5, s6)
+    # the same on a non-default stream
+    for kw in ({}, {"want_state": False}, {"alias": True}):
+        o7, s7 = _run_capped(x, dtype, C, cap, side=True, **kw)
+        np.testing.assert_array_equal(o1, o7)
+        if s7 is not None:
+            np.testing.assert_array_equal(s1, s7)
     o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
     assert rel_err(o2, o_ref) <= TOL[dtype] and rel_err(s2, s_ref) <= TOL[dtype]
