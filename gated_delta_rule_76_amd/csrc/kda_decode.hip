@@ -65,7 +65,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
   for (int m = 0; m < Sh::RPT; ++m) s[m] = S4[(rg + Sh::RG * m) * Sh::CG + cg];
 
   __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
-  __shared__ float red[Sh::NW][2 * DV + 1];
+  // per-wave partial reductions, one float4 per column group (16-byte
+  // accesses: one LDS write per lane, no bank conflicts)
+  __shared__ float4 red_y[Sh::NW][Sh::CG], red_z[Sh::NW][Sh::CG];
+  __shared__ float red_kq[Sh::NW];
   // gate: one decay per channel, one per head (broadcast), or none; with the
   // fused prologue the gate and beta arrive as raw projections
   float ah = gate == kGateHead ? load_scalar(alpha, head) : 1.f;
@@ -126,21 +129,18 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
   if constexpr (Sh::NW > 1) {
     const int lane = tid & 63, w = tid >> 6;
     if (lane < Sh::CG) {
-      float* r = red[w];
-      r[4 * cg + 0] = y0; r[4 * cg + 1] = y1; r[4 * cg + 2] = y2; r[4 * cg + 3] = y3;
-      r[DV + 4 * cg + 0] = z0; r[DV + 4 * cg + 1] = z1;
-      r[DV + 4 * cg + 2] = z2; r[DV + 4 * cg + 3] = z3;
-      if (cg == 0) r[2 * DV] = kq;
+      red_y[w][cg] = float4{y0, y1, y2, y3};
+      red_z[w][cg] = float4{z0, z1, z2, z3};
+      if (cg == 0) red_kq[w] = kq;
     }
     __syncthreads();
     y0 = y1 = y2 = y3 = z0 = z1 = z2 = z3 = kq = 0.f;
 #pragma unroll
     for (int ww = 0; ww < Sh::NW; ++ww) {
-      const float* r = red[ww];
-      y0 += r[4 * cg + 0]; y1 += r[4 * cg + 1]; y2 += r[4 * cg + 2]; y3 += r[4 * cg + 3];
-      z0 += r[DV + 4 * cg + 0]; z1 += r[DV + 4 * cg + 1];
-      z2 += r[DV + 4 * cg + 2]; z3 += r[DV + 4 * cg + 3];
-      kq += r[2 * DV];
+      const float4 ry = red_y[ww][cg], rz = red_z[ww][cg];
+      y0 += ry.x; y1 += ry.y; y2 += ry.z; y3 += ry.w;
+      z0 += rz.x; z1 += rz.y; z2 += rz.z; z3 += rz.w;
+      kq += red_kq[ww];
     }
   }
   if (rule == kRuleLinear) y0 = y1 = y2 = y3 = 0.f;  // no correction: u = beta v

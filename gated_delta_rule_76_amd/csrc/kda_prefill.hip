@@ -414,7 +414,15 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       const float bx = load_scalar(&rb, 0);
       sm.beta[tid] = tid < valid ? (fused ? sigmoid_f(bx) : bx) : 0.f;
     }
+
     __syncthreads();
+    // The tiles below divide by the cumulative decay gamma_r, which must stay
+    // in the normal fp32 range.  With alpha in (0, 1] gamma_r falls with r,
+    // so the chunk's whole decay gamma_C decides: a chunk with gamma_C below
+    // 2^-126 in some channel (an alpha of 0, or a product over the chunk
+    // below about e^-87) is outside the chunked form's domain.  It is flagged
+    // and gets NaN write strengths (Tm), so its outputs, the state and all
+    // later outputs of the chain come out NaN instead of silently wrong.
     if (tid < DK) {  // exclusive products of the row-group totals, per channel
       float tot[P::NRG];
 #pragma unroll
@@ -426,6 +434,13 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         p *= tot[gg];
       }
       sm.gC[tid] = p;
+      if (!(p >= 0x1p-126f)) {
+        // beta = NaN makes Tm = X Diag(beta) NaN (beta is next read after
+        // phase 3; every thread that finds the chunk out of range writes
+        // the same values)
+        const float nan = __builtin_nanf("");
+        for (int i = 0; i < C; i += 4) *reinterpret_cast<f32x4*>(&sm.beta[i]) = f32x4{nan, nan, nan, nan};
+      }
     }
     __syncthreads();
     f32x8 pre, gc;
@@ -755,12 +770,14 @@ struct PassCfg {
 //   state: R = V - K+ S, U = Tm R, publish U, S <- gamma_C S + Kbar^T U,
 //          publish the next state operand
 //   output: O = Q+ S (before U is ready), then + P U, into the output tile
-template <typename E, int DK, int DVB, int C>
+// DELTA: the error-correcting write (R = V - K+ S); without it R = V.  A
+// template parameter, so that each kernel holds one chain loop.
+template <typename E, int DK, int DVB, int C, bool DELTA>
 __global__ __launch_bounds__((PassCfg<E, DK, DVB, C>::NTH))
 __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, DVB, C>::WPE))) void state_pass_kernel(
     const char* __restrict__ ws, const typename E::storage* __restrict__ v,
     const float* __restrict__ S0, typename E::storage* __restrict__ o, float* __restrict__ ST,
-    int T, int H, int DV, int n0, int nchunk, int rule, int wait_limit) {
+    int T, int H, int DV, int n0, int nchunk, int wait_limit) {
   using S = Shape<E, DK, C>;
   using K = PassCfg<E, DK, DVB, C>;
   using M = typename S::M;
@@ -879,8 +896,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     // one batch with a single LDS wait (see lds_read16).
     constexpr bool FAST = std::is_same<E, Bf16>::value && S::NT * S::NKS == 16 && S::NTRI == 6 &&
                           S::NTK == 8 && S::NTK * S::NCS == 16 && S::FRAG == 1024;
-    auto chain_step = [&](int n, auto delta_rule) {
-      constexpr bool DELTA = decltype(delta_rule)::value;
+    auto chain_step = [&](int n) {
       const int t0 = (n0 + n) * C;
       const char* sl = slot_of(n);
       auto fr = [&](int off, int idx) -> frag {
@@ -992,18 +1008,11 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
         xn[s2 * 64 + lane] = sfr[s2];
       }
     };
-    // one loop per update rule, so that neither shares code with the other
-    auto run_chain = [&](auto delta_rule) {
-      for (int n = 0; n < nchunk; ++n) {
-        __syncthreads();  // [A]
-        chain_step(n, delta_rule);
-        if (K::NBUF == 1) __syncthreads();  // [B]
-      }
-    };
-    if (rule == kRuleDelta)
-      run_chain(std::true_type{});
-    else
-      run_chain(std::false_type{});
+    for (int n = 0; n < nchunk; ++n) {
+      __syncthreads();  // [A]
+      chain_step(n);
+      if (K::NBUF == 1) __syncthreads();  // [B]
+    }
     if (nchunk > 0) __syncthreads();  // final [A]
     if (ST != nullptr) {
       float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
@@ -1150,9 +1159,9 @@ int num_cus() {
 
 // State pass with value blocks of DVB columns: one workgroup per (chain,
 // value block), over chunks n0 .. n0 + cnt - 1.
-template <typename E, int DK, int DVB, int C>
-hipError_t launch_pass(const PrefillArgs& a, const char* ws, int n0, int cnt, const float* s_in,
-                       float* s_out) {
+template <typename E, int DK, int DVB, int C, bool DELTA>
+hipError_t launch_pass_rule(const PrefillArgs& a, const char* ws, int n0, int cnt,
+                            const float* s_in, float* s_out) {
   using St = typename E::storage;
   using K = PassCfg<E, DK, DVB, C>;
   // Opt in to more than 64 KiB of LDS, once per device (bit d of the mask;
@@ -1163,7 +1172,7 @@ hipError_t launch_pass(const PrefillArgs& a, const char* ws, int n0, int cnt, co
   if (e != hipSuccess) return e;
   const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
   if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    const void* fn = reinterpret_cast<const void*>(&state_pass_kernel<E, DK, DVB, C>);
+    const void* fn = reinterpret_cast<const void*>(&state_pass_kernel<E, DK, DVB, C, DELTA>);
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(K::smem_bytes));
     if (e != hipSuccess) return e;
@@ -1172,11 +1181,17 @@ hipError_t launch_pass(const PrefillArgs& a, const char* ws, int n0, int cnt, co
   // grid.x = (batch, head) chains, grid.y = value blocks: the value blocks
   // of one chain are gridDim.x apart in dispatch order, which keeps them on
   // one XCD (and its L2) whenever gridDim.x is a multiple of 8.
-  hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C>), dim3(a.B * a.H, a.d_v / DVB),
+  hipLaunchKernelGGL((state_pass_kernel<E, DK, DVB, C, DELTA>), dim3(a.B * a.H, a.d_v / DVB),
                      dim3(K::NTH), K::smem_bytes, a.stream, ws, static_cast<const St*>(a.v),
-                     s_in, static_cast<St*>(a.o), s_out, a.T, a.H, a.d_v, n0, cnt, a.rule,
-                     wait_limit());
+                     s_in, static_cast<St*>(a.o), s_out, a.T, a.H, a.d_v, n0, cnt, wait_limit());
   return hipGetLastError();
+}
+
+template <typename E, int DK, int DVB, int C>
+hipError_t launch_pass(const PrefillArgs& a, const char* ws, int n0, int cnt, const float* s_in,
+                       float* s_out) {
+  return a.rule == kRuleDelta ? launch_pass_rule<E, DK, DVB, C, true>(a, ws, n0, cnt, s_in, s_out)
+                              : launch_pass_rule<E, DK, DVB, C, false>(a, ws, n0, cnt, s_in, s_out);
 }
 
 template <typename E, int DK, int C>

@@ -116,10 +116,15 @@ KDA_API const char *kda_status_string(int status);
  * Semantics: T = 0 copies S0 (or zeros) to S_T and leaves o untouched.  A
  * last chunk shorter than `chunk` is handled exactly (padding tokens write
  * nothing and do not decay the state).
- * Precondition of the chunked form: 0 < alpha <= 1 and, per channel, the
- * product of alpha over any chunk stays above exp(-80) (fp32 range of the
- * per-chunk decay factors).  Other gate values give unspecified results; the
- * decode call below has no such restriction.
+ * Range of the chunked form: 0 < alpha <= 1 and, per channel, the product
+ * of alpha over the tokens of any chunk at least 2^-126 (about e^-87.3; the
+ * chunk's decay factors are fp32).  A chunk outside that range (an alpha of
+ * exactly 0, or decays that strong) is detected: its chain's outputs from the
+ * start of that chunk on and its S_T come out NaN, and the other chains are
+ * unaffected.  A smaller chunk widens the range per token (chunk 16 allows
+ * four times the per-token decay of chunk 64).  alpha > 1 gives unspecified
+ * results.  The decode call below has no such restriction (exact for alpha =
+ * 0).
  */
 KDA_API int kda_fwd_chunked(const void *q, const void *k, const void *v, const void *alpha,
                     const void *beta, const float *S0, void *o, float *S_T,
@@ -157,7 +162,11 @@ KDA_API int kda_fwd_chunked_ex(const void *q, const void *k, const void *v, cons
  *   b_raw        : [B, T, H] dtype; beta = sigmoid(b_raw) = 1 / (1 + e^-b_raw)
  *   gate_scale   : c >= 0, finite; otherwise KDA_ERR_INVALID_ARG
  * v is used as given.  All other arguments, the workspace and the semantics
- * are those of kda_fwd_chunked_ex.
+ * are those of kda_fwd_chunked_ex.  Safe range of the raw gate (the range
+ * of the chunked form above): per channel, c * sum softplus(g_raw) over the
+ * tokens of any chunk at most 87; on average c * softplus(g_raw) <= 1.36 at
+ * chunk 64, <= 2.7 at chunk 32, <= 5.4 at chunk 16 (softplus(0) = 0.69).
+ * Chunks beyond it give NaN as described for kda_fwd_chunked.
  */
 KDA_API int kda_fwd_chunked_fused(const void *q_raw, const void *k_raw, const void *v,
                           const void *g_raw, const void *b_raw, float gate_scale,

@@ -224,3 +224,123 @@ def test_variants_32_column_blocks(gate, rule):
         es = rel_err(st[bb:bb + 1, hh:hh + 1], s_ref)
         log(f"  chain ({bb},{hh}): rel_err o {eo:.2e}  S_T {es:.2e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ---------------------------------------------------- strong decays, range edge
+def _chunk_log_decay(alpha, C):
+    """Per (batch, chunk, head, channel): the sum of log alpha over the
+    chunk's tokens, in fp64 (-inf where an alpha is 0)."""
+    a = np.asarray(alpha, dtype=np.float64)
+    B, T, H, D = a.shape
+    n = (T + C - 1) // C
+    pad = np.ones((B, n * C - T, H, D))
+    with np.errstate(divide="ignore"):
+        la = np.log(np.concatenate([a, pad], axis=1))
+    return la.reshape(B, n, C, H, D).sum(axis=2)
+
+
+# In range means every chunk's decay stays above e^-80 in every channel (the
+# kernels need 2^-126 ~ e^-87.3; the margin keeps fp32 rounding away from it).
+STRONG = [
+    # dtype, d_k, d_v, C, B, T, H, gate_scale
+    ("bf16", 128, 128, 64, 2, 300, 2, 1.0),
+    ("bf16", 128, 128, 16, 1, 250, 3, 2.0),
+    ("bf16", 64, 64, 32, 2, 200, 2, 1.5),
+    ("f32", 64, 64, 16, 1, 150, 2, 3.0),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,C,B,T,H,c", STRONG)
+def test_fused_strong_gates_in_range(dtype, dk, dv, C, B, T, H, c):
+    """Fused prologue with gate scales of 1 to 3 (per-token decays down to
+    e^-10 and below): where every chunk's decay stays in range, the chunked
+    prefill matches the oracle."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    log(f"[strong gates] fused {dtype} dk{dk} dv{dv} C{C} B{B} T{T} H{H} gate_scale {c}")
+    x = raw_prefill_inputs(B, T, H, dk, dv, dtype=dtype, s0_std=0.05, seed=int(c * 10) + C)
+    _, _, alpha, _ = oracle.input_prologue(x["q_raw"], x["k_raw"], x["g_raw"], x["b_raw"], c)
+    lmin = float(_chunk_log_decay(alpha, C).min())
+    log(f"  smallest chunk log-decay {lmin:.1f}; smallest alpha {float(alpha.min()):.2e}")
+    assert lmin > -80.0, "test inputs must stay inside the chunked form's range"
+    q, k, v, g, b = (to_dev(x[n], dtype) for n in ("q_raw", "k_raw", "v", "g_raw", "b_raw"))
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o, st = kda.kda_fwd_chunked_fused(q, k, v, g, b, s0, gate_scale=c, chunk=C)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_forward_fused(x["q_raw"], x["k_raw"], x["v"], x["g_raw"], x["b_raw"],
+                                            x["S0"], gate_scale=c)
+    eo, es = rel_err(to_np(o), o_ref), rel_err(to_np(st), s_ref)
+    log(f"  rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("bf16", 16), ("f32", 32)])
+def test_near_zero_decays_in_range(dtype, C):
+    """Single tokens whose gate nearly closes (alpha = 1e-12 in some channels)
+    inside otherwise ordinary gates: in range, so the oracle is matched."""
+    log(f"[near-zero decays] {dtype} dk128 C{C} B2 T260 H2")
+    x = prefill_inputs(2, 260, 2, 128, 128, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=41 + C)
+    rng = np.random.default_rng(5)
+    a = x["alpha"]
+    for t in rng.choice(260, size=6, replace=False):
+        ch = rng.choice(128, size=40, replace=False)
+        a[:, t, :, ch] = 1e-12
+    if dtype == "bf16":
+        from synth import round_to_bf16
+        x["alpha"] = round_to_bf16(a)
+    assert float(_chunk_log_decay(x["alpha"], C).min()) > -80.0
+    o, st = _prefill(x, dtype, C, "channel", "delta")
+    o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(st, s_ref)
+    log(f"  rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("f32", 32)])
+def test_out_of_range_chunk_turns_its_chain_nan(dtype, C):
+    """An alpha of exactly 0 puts its chunk outside the chunked form's range.
+    The documented outcome: that chain's outputs from the start of the chunk
+    on, and its final state, are NaN; earlier outputs and every other chain
+    still match the oracle (which handles alpha = 0 exactly)."""
+    B, T, H = 2, 300, 3
+    log(f"[out of range] {dtype} dk128 C{C} B{B} T{T} H{H}, alpha = 0 at (b=1, t=150, h=2)")
+    x = prefill_inputs(B, T, H, 128, 128, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=43)
+    t0, n0 = 150, (150 // C) * C
+    x["alpha"][1, t0, 2, 7] = 0.0
+    o, st = _prefill(x, dtype, C, "channel", "delta")
+    o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    assert np.all(np.isnan(o[1, n0:, 2])) and np.all(np.isnan(st[1, 2]))
+    assert np.all(np.isfinite(o[1, :n0, 2]))
+    good_o = np.concatenate([o[0].reshape(-1), o[1, :, :2].reshape(-1), o[1, :n0, 2].reshape(-1)])
+    ref_o = np.concatenate([o_ref[0].reshape(-1), o_ref[1, :, :2].reshape(-1),
+                            o_ref[1, :n0, 2].reshape(-1)])
+    good_s = np.concatenate([st[0].reshape(-1), st[1, :2].reshape(-1)])
+    ref_s = np.concatenate([s_ref[0].reshape(-1), s_ref[1, :2].reshape(-1)])
+    eo, es = rel_err(good_o, ref_o), rel_err(good_s, ref_s)
+    log(f"  other outputs: rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_fused_gates_beyond_range_are_nan():
+    """Gate scale 3 at chunk 64 takes every chunk's decay below e^-87: every
+    output and the final state come back NaN (the documented outcome), and
+    the same inputs at chunk 16 stay in range and match the oracle."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    B, T, H, d, c = 1, 192, 2, 64, 3.0
+    log(f"[beyond range] fused bf16 d{d} B{B} T{T} H{H} gate_scale {c}, chunks 64 and 16")
+    x = raw_prefill_inputs(B, T, H, d, d, dtype="bf16", s0_std=0.05, seed=47)
+    _, _, alpha, _ = oracle.input_prologue(x["q_raw"], x["k_raw"], x["g_raw"], x["b_raw"], c)
+    assert float(_chunk_log_decay(alpha, 64).max()) < -95.0
+    assert float(_chunk_log_decay(alpha, 16).min()) > -80.0
+    q, k, v, g, b = (to_dev(x[n], "bf16") for n in ("q_raw", "k_raw", "v", "g_raw", "b_raw"))
+    s0 = torch.from_numpy(x["S0"]).cuda()
+    o64, st64 = kda.kda_fwd_chunked_fused(q, k, v, g, b, s0, gate_scale=c, chunk=64)
+    o16, st16 = kda.kda_fwd_chunked_fused(q, k, v, g, b, s0, gate_scale=c, chunk=16)
+    torch.cuda.synchronize()
+    assert torch.isnan(o64.float()).all().item() and torch.isnan(st64).all().item()
+    o_ref, s_ref = oracle.kda_forward_fused(x["q_raw"], x["k_raw"], x["v"], x["g_raw"], x["b_raw"],
+                                            x["S0"], gate_scale=c)
+    eo, es = rel_err(to_np(o16), o_ref), rel_err(to_np(st16), s_ref)
+    log(f"  chunk 16: rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
