@@ -1,7 +1,9 @@
 """Build libkda.so (the HIP library behind include/kda.h) for gfx950.
 
 Each .hip translation unit is compiled with hipcc in parallel, then linked
-into gated_delta_rule_76_amd/libkda.so.  Usage: python -m gated_delta_rule_76_amd.build
+into gated_delta_rule_76_amd/libkda.so.  The benchmark's calibration kernels
+(csrc/calibrate.hip) go into a separate libkda_calibrate.so, outside the KDA
+C ABI.  Usage: python -m gated_delta_rule_76_amd.build
 """
 from __future__ import annotations
 
@@ -16,9 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
+CALIB_LIB = os.path.join(PKG, "libkda_calibrate.so")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "attnres.hip"]
+CALIB_SOURCES = ["calibrate.hip"]
 
 # -packed-fp32-ops off: every fp32 op stays scalar VALU (no v_pk_*_f32).
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=hidden",
@@ -47,18 +51,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _link(objs, lib: str) -> None:
+    tmp = lib + f".tmp{os.getpid()}"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 
