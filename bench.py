@@ -36,6 +36,7 @@ METRIC = "KDA prefill tokens/s (H=16,d=128) + decode state-update HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PREFILL = "prefill_b4_h16_t16k"
+SMALL = "prefill_h8_t4k"
 LONG = "prefill_h16_t128k"
 DECODE = "decode_b256_h16"
 
@@ -485,6 +486,7 @@ _TRACE_PHASES = [("prefill_b4_h16_t16k", ("chunk_prep_kernel", "state_pass_kerne
                  ("mfma calibration", ("mfma16_loop", "mfma32_loop"), 1),
                  ("decode_b256_h16", ("decode_kernel",), 1),
                  ("prefill_h16_t128k", ("chunk_prep_kernel", "state_pass_kernel"), 8),
+                 ("prefill_h8_t4k", ("chunk_prep_kernel", "state_pass_kernel"), 1),
                  ("prefill_b4_h16_t16k (per-head gate)", ("chunk_prep_kernel", "state_pass_kernel"), 4),
                  ("attnres_l64_n4096_d4096", ("attnres_kernel",), 1)]
 
@@ -566,6 +568,7 @@ def main():
                     help="decode steps (all heads) the CPU baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-attnres", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
@@ -668,6 +671,17 @@ def main():
                                "chunk": wl.chunk},
                     "hbm_frac": round(lby / (l_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # B1 H8 T4K: 8 chains of 64 chunks, a launch-latency-sized call
+    small = None
+    if not args.no_small:
+        ws_, stot, sper, ok_s = bench_prefill(SMALL, 4 * args.steps, args.warmup)
+        sby = prefill_alg_bytes(ws_.B, ws_.T, ws_.H, ws_.d_k, ws_.d_v)
+        small = {"value": round(ws_.B * ws_.T * 4 * args.steps / stot, 1), "unit": "tokens/s",
+                 "ms_per_call": round(sper, 4), "finite": ok_s,
+                 "config": {"workload": SMALL, "batch": ws_.B, "seq_len": ws_.T, "heads": ws_.H,
+                            "chunk": ws_.chunk},
+                 "hbm_frac": round(sby / (sper / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # Gated DeltaNet variant (one decay per token and head) on the headline shape
     gdn = None
     if not args.no_gdn:
@@ -712,6 +726,7 @@ def main():
                    "d_k": w.d_k, "d_v": w.d_v, "chunk": w.chunk, "state": "fp32",
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "decode": decode, "long_context": long_ctx,
+        "small_prefill": small,
         "gated_deltanet": gdn, "attnres": attnres,
         "finite": bool(ok_p and ok_d),
     }
