@@ -115,7 +115,11 @@ KDA_API const char *kda_status_string(int status);
  *
  * Semantics: T = 0 copies S0 (or zeros) to S_T and leaves o untouched.  A
  * last chunk shorter than `chunk` is handled exactly (padding tokens write
- * nothing and do not decay the state).
+ * nothing and do not decay the state).  A NaN or Inf in a chain's inputs at
+ * token t makes that chain's outputs from t on and its S_T non-finite;
+ * outputs of t's chunk before t may be non-finite too (the chunk's tokens
+ * are combined in matrix products), earlier chunks and other chains are
+ * unaffected.  In decode a non-finite input stays in its (batch, head).
  * Range of the chunked form: 0 < alpha <= 1 and, per channel, the product
  * of alpha over the tokens of any chunk at least 2^-126 (about e^-87.3; the
  * chunk's decay factors are fp32).  A chunk outside that range (an alpha of

@@ -401,3 +401,52 @@ def test_segmented_prefill_is_bitwise_the_single_pass(dtype, dk, dv, C, B, T, H,
             np.testing.assert_array_equal(s1, s7)
     o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
     assert rel_err(o2, o_ref) <= TOL[dtype] and rel_err(s2, s_ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,C,bad", [("bf16", 64, "nan"), ("f32", 32, "inf")])
+def test_nonfinite_input_propagation(dtype, C, bad):
+    """A NaN or Inf in one chain's key at token t: that chain's outputs from
+    token t on and its final state are non-finite (rows of t's chunk before t
+    may be too: the chunk's matrix products mix its rows); its earlier chunks
+    and every other chain match the oracle."""
+    B, T, H = 2, 260, 2
+    t0 = 150
+    n0 = (t0 // C) * C
+    log(f"[non-finite input] {dtype} C{C}: k[1, {t0}, 0, 5] = {bad}")
+    x = prefill_inputs(B, T, H, 128, 128, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=51)
+    x["k"][1, t0, 0, 5] = np.float32(bad)
+    o, st = run_prefill(x, dtype, C)
+    o_ref, s_ref = oracle.kda_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["S0"])
+    assert not np.any(np.isfinite(o[1, t0:, 0])) and not np.any(np.isfinite(st[1, 0]))
+    keep_o = [o[0], o[1, :, 1], o[1, :n0, 0]]
+    keep_r = [o_ref[0], o_ref[1, :, 1], o_ref[1, :n0, 0]]
+    eo = rel_err(np.concatenate([a.ravel() for a in keep_o]),
+                 np.concatenate([a.ravel() for a in keep_r]))
+    es = rel_err(np.concatenate([st[0].ravel(), st[1, 1].ravel()]),
+                 np.concatenate([s_ref[0].ravel(), s_ref[1, 1].ravel()]))
+    log(f"  unaffected outputs: rel_err o {eo:.2e}  S_T {es:.2e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_nonfinite_decode_input_stays_in_its_head():
+    """Decode: a NaN in one head's key makes that head's output and state NaN;
+    every other head matches the oracle."""
+    import torch
+    kda = _kda()
+    from synth import decode_pool
+    B, H, d = 3, 4, 64
+    log(f"[non-finite decode input] bf16 B{B} H{H} d{d}: k[2, 1, 9] = nan")
+    p = decode_pool(B, H, d, d, pool=1, dtype="bf16", gate_c=0.1, s0_std=0.05, seed=52)
+    p["k"][0, 2, 1, 9] = np.nan
+    q, k, v, a, b = (to_dev(p[n][0], "bf16") for n in ("q", "k", "v", "alpha", "beta"))
+    S = torch.from_numpy(p["S"]).cuda()
+    o = kda.kda_decode_step(q, k, v, a, b, S)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_decode_step(p["q"][0], p["k"][0], p["v"][0], p["alpha"][0],
+                                          p["beta"][0], p["S"])
+    o_np, s_np = to_np(o), to_np(S)
+    assert np.all(np.isnan(o_np[2, 1])) and np.all(np.isnan(s_np[2, 1]))
+    mask = np.ones((B, H), bool)
+    mask[2, 1] = False
+    assert rel_err(o_np[mask], o_ref[mask]) <= TOL["bf16"]
+    assert rel_err(s_np[mask], s_ref[mask]) <= TOL["bf16"]
