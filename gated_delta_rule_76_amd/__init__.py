@@ -31,17 +31,20 @@ KDA_BF16 = 1
 GATES = {"channel": 0, "head": 1, "none": 2}
 RULES = {"delta": 0, "linear": 1}
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
-          3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP"}
+          3: "KDA_ERR_WORKSPACE", 4: "KDA_ERR_HIP", 5: "KDA_ERR_CHECK"}
 # Every symbol include/kda.h declares.
 ABI_SYMBOLS = ("kda_version", "kda_status_string", "kda_fwd_chunked", "kda_fwd_chunked_ex",
                "kda_fwd_chunked_fused", "kda_fwd_chunked_workspace_bytes", "kda_decode_step",
                "kda_decode_step_ex", "kda_decode_step_fused", "attnres_forward",
                "kda_fwd_chunked_noalloc",
                "kda_testing_set_wait_limit", "kda_testing_wait_limit",
-               "kda_testing_set_ring_cap", "kda_testing_ring_cap")
+               "kda_testing_set_ring_cap", "kda_testing_ring_cap",
+               "kda_build_checked", "kda_check_sites", "kda_testing_check_probe")
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libkda.so")
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+CHECKED_LIB_PATH = os.path.join(_PKG, "libkda_checked.so")  # bounds-checked debugging build
+_LIB_PATH = LIB_PATH
 _lib = None
 
 
@@ -52,6 +55,18 @@ class KdaError(RuntimeError):
 
 
 def library_path() -> str:
+    return _LIB_PATH
+
+
+def select_build(checked: bool = False) -> str:
+    """Route every later call through libkda.so (default) or the
+    bounds-checked debugging build libkda_checked.so (include/kda.h, "Checked
+    build": synchronous, returns KDA_ERR_CHECK if a kernel index leaves its
+    buffer).  Returns the library path now in use."""
+    global _LIB_PATH, _lib
+    path = CHECKED_LIB_PATH if checked else LIB_PATH
+    if path != _LIB_PATH:
+        _LIB_PATH, _lib = path, None
     return _LIB_PATH
 
 
@@ -99,6 +114,12 @@ def lib() -> ctypes.CDLL:
         L.kda_testing_set_ring_cap.restype = i
         L.kda_testing_ring_cap.argtypes = []
         L.kda_testing_ring_cap.restype = sz
+        L.kda_build_checked.argtypes = []
+        L.kda_build_checked.restype = i
+        L.kda_check_sites.argtypes = []
+        L.kda_check_sites.restype = ctypes.c_uint
+        L.kda_testing_check_probe.argtypes = [vp]
+        L.kda_testing_check_probe.restype = i
         _lib = L
     return _lib
 
@@ -130,6 +151,22 @@ def set_ring_cap(nbytes: int) -> int:
 
 def ring_cap() -> int:
     return int(lib().kda_testing_ring_cap())
+
+
+def build_checked() -> bool:
+    """True when the library in use is the bounds-checked build."""
+    return bool(lib().kda_build_checked())
+
+
+def check_sites() -> int:
+    """Site mask of the last call that returned KDA_ERR_CHECK (checked build)."""
+    return int(lib().kda_check_sites())
+
+
+def check_probe(stream=None) -> int:
+    """Test hook: one bounds check that fails on purpose without touching
+    memory; KDA_ERR_CHECK (5) in the checked build, 0 otherwise."""
+    return int(lib().kda_testing_check_probe(stream))
 
 
 def status_string(status: int) -> str:

@@ -1,7 +1,9 @@
 """Build libkda.so (the HIP library behind include/kda.h) for gfx950.
 
 Each .hip translation unit is compiled with hipcc in parallel, then linked
-into gated_delta_rule_76_amd/libkda.so.  The benchmark's calibration kernels
+into gated_delta_rule_76_amd/libkda.so; the same units compiled with
+-DKDA_CHECKED=1 (bounds checks in every kernel) are linked into
+libkda_checked.so, a debugging build.  The benchmark's calibration kernels
 (csrc/calibrate.hip) go into a separate libkda_calibrate.so, outside the KDA
 C ABI.  Usage: python -m gated_delta_rule_76_amd.build
 """
@@ -18,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
+CHECKED_LIB = os.path.join(PKG, "libkda_checked.so")
 CALIB_LIB = os.path.join(PKG, "libkda_calibrate.so")
 ARCH = "gfx950"
 
@@ -37,9 +40,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libkda.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, checked = job
+    sub = os.path.join(BUILD, "checked") if checked else BUILD
+    obj = os.path.join(sub, os.path.splitext(src)[0] + ".o")
+    extra = ["-DKDA_CHECKED=1"] if checked else []
+    cmd = [hipcc()] + CFLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass reports the device-only feature flag as unknown: harmless
     noise = "is not a recognized feature for this target"
@@ -61,14 +67,19 @@ def _link(objs, lib: str) -> None:
 
 
 def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + CALIB_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], CALIB_LIB)
+    """Build libkda.so, its bounds-checked twin libkda_checked.so (the same
+    sources with -DKDA_CHECKED=1) and libkda_calibrate.so."""
+    os.makedirs(os.path.join(BUILD, "checked"), exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in SOURCES] + \
+           [(s, False) for s in CALIB_SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:2 * n], CHECKED_LIB)
+    _link(objs[2 * n:], CALIB_LIB)
     if verbose:
-        print(f"built {LIB} and {CALIB_LIB}")
+        print(f"built {LIB}, {CHECKED_LIB} and {CALIB_LIB}")
     return LIB
 
 

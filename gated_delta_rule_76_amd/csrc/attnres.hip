@@ -15,13 +15,19 @@
 #include <stdint.h>
 
 #include "../../include/attnres.h"
+#include "kda_check.h"
 #include "kda_device.h"
+#include "kda_internal.h"
 
 namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxLayers = 1024;
+
+// Check sites of this unit (bits of the checked build's failure mask, before
+// the unit's shift).
+enum : int { kSiteQ = 0, kSiteK = 1, kSiteH = 2, kSiteOut = 3 };
 
 // The layer outputs are read once per call: streaming (nontemporal) loads
 // keep them from displacing other lines in the caches.
@@ -81,13 +87,16 @@ __global__ __launch_bounds__(kThreads) void attnres_kernel(
   __shared__ float red[2];
   const long n = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // extents for the checked build
+  const long nq = static_cast<long>(N) * dk, nk = nq * L, nh = static_cast<long>(L) * N * d;
+  const long no = static_cast<long>(N) * d;
 
   // 1. scores q . k_i
   for (int i = wave; i < L; i += kThreads / 64) {
-    const St* ki = k + (static_cast<long>(i) * N + n) * dk;
-    const St* qn = q + n * dk;
+    const long ki = (static_cast<long>(i) * N + n) * dk;
     float s = 0.f;
-    for (int c = lane; c < dk; c += 64) s += load_scalar(qn, c) * load_scalar(ki, c);
+    for (int c = lane; c < dk; c += 64)
+      s += load_scalar(q, chk(n * dk + c, nq, kSiteQ)) * load_scalar(k, chk(ki + c, nk, kSiteK));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) w[i] = s;
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void attnres_kernel(
   // 3. weighted sum of the layer outputs: two column groups per thread and
   //    four layers per step keep eight 16-byte loads in flight
   const long rowstride = static_cast<long>(N) * d;  // between layers
-  const St* hn = h + n * d;
+  const long hn = n * d;
   for (int c0 = 8 * tid; c0 < d; c0 += 16 * kThreads) {
     const int c1 = c0 + 8 * kThreads;
     const bool two = c1 < d;
@@ -126,8 +135,8 @@ __global__ __launch_bounds__(kThreads) void attnres_kernel(
       Vec8<St> x[4], y[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[j].load(hn + (i + j) * rowstride + c0);
-        y[j].load(hn + (i + j) * rowstride + c1s);
+        x[j].load(h + chk(hn + (i + j) * rowstride + c0, nh, kSiteH, 8));
+        y[j].load(h + chk(hn + (i + j) * rowstride + c1s, nh, kSiteH, 8));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -137,15 +146,15 @@ __global__ __launch_bounds__(kThreads) void attnres_kernel(
     }
     for (; i < L; ++i) {
       Vec8<St> x, y;
-      x.load(hn + i * rowstride + c0);
-      y.load(hn + i * rowstride + c1s);
+      x.load(h + chk(hn + i * rowstride + c0, nh, kSiteH, 8));
+      y.load(h + chk(hn + i * rowstride + c1s, nh, kSiteH, 8));
       x.fma(w[i], a0);
       y.fma(w[i], a1);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) { a0[e] *= inv; a1[e] *= inv; }
-    Vec8<St>::store(out + n * d + c0, a0);
-    if (two) Vec8<St>::store(out + n * d + c1, a1);
+    if (chk_ok(n * d + c0, no, kSiteOut, 8)) Vec8<St>::store(out + n * d + c0, a0);
+    if (two && chk_ok(n * d + c1, no, kSiteOut, 8)) Vec8<St>::store(out + n * d + c1, a1);
   }
 }
 
@@ -157,6 +166,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 }  // namespace
+
+unsigned attnres_check_take() { return check_take(); }
+
 }  // namespace kda
 
 extern "C" int attnres_forward(const void* q, const void* k, const void* h, void* out, int L, int N,
@@ -181,7 +193,8 @@ extern "C" int attnres_forward(const void* q, const void* k, const void* h, void
       hipLaunchKernelGGL(attnres_kernel<F32>, dim3(N), dim3(kThreads), 0, s,
                          static_cast<const float*>(q), static_cast<const float*>(k),
                          static_cast<const float*>(h), static_cast<float*>(out), L, N, d_k, d);
-    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    return checked_finish(s, KDA_OK);
   } catch (...) {
     return KDA_ERR_HIP;
   }

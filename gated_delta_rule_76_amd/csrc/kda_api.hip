@@ -6,6 +6,7 @@
 
 #include "../../include/kda.h"
 #include "../../include/kda_testing.h"
+#include "kda_check.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -13,10 +14,20 @@ namespace kda {
 namespace {
 std::atomic<int> g_wait_limit{1 << 24};
 std::atomic<size_t> g_ring_cap{kRingCap};
+std::atomic<unsigned> g_check_sites_last{0};  // checked build: mask of the last failed call
 }  // namespace
 
 int wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
 size_t ring_cap() { return g_ring_cap.load(std::memory_order_relaxed); }
+
+int checked_finish(hipStream_t stream, int status) {
+  if (!kChecked || status != KDA_OK) return status;
+  if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+  const unsigned m = prefill_check_take() | (decode_check_take() << 16) | (attnres_check_take() << 24);
+  if (m == 0) return KDA_OK;
+  g_check_sites_last.store(m, std::memory_order_relaxed);
+  return KDA_ERR_CHECK;
+}
 
 }  // namespace kda
 
@@ -58,6 +69,20 @@ int kda_testing_set_ring_cap(size_t bytes) {
 
 size_t kda_testing_ring_cap(void) { return kda::ring_cap(); }
 
+int kda_testing_check_probe(void* stream) {
+  try {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::launch_check_probe(s) != hipSuccess) return KDA_ERR_HIP;
+    return kda::checked_finish(s, KDA_OK);
+  } catch (...) {
+    return KDA_ERR_HIP;
+  }
+}
+
+int kda_build_checked(void) { return kda::kChecked ? 1 : 0; }
+
+unsigned int kda_check_sites(void) { return kda::g_check_sites_last.load(std::memory_order_relaxed); }
+
 const char* kda_status_string(int status) {
   switch (status) {
     case KDA_OK: return "KDA_OK";
@@ -65,6 +90,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_CHECK: return "KDA_ERR_CHECK";
   }
   return "KDA_ERR_UNKNOWN";
 }
@@ -144,7 +170,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* alpha, con
     a.workspace_bytes = workspace_bytes;
     a.ring_cap = cap;
     a.stream = static_cast<hipStream_t>(stream);
-    return from_hip(noalloc ? kda::launch_prefill_noalloc(a) : kda::launch_prefill(a));
+    return kda::checked_finish(a.stream, from_hip(noalloc ? kda::launch_prefill_noalloc(a)
+                                                           : kda::launch_prefill(a)));
   } catch (...) {
     return KDA_ERR_HIP;
   }
@@ -177,7 +204,7 @@ int decode_impl(const void* q, const void* k, const void* v, const void* alpha, 
     a.fused = fused; a.gate_scale = gate_scale;
     a.bf16 = dtype == KDA_BF16;
     a.stream = static_cast<hipStream_t>(stream);
-    return from_hip(kda::launch_decode(a));
+    return kda::checked_finish(a.stream, from_hip(kda::launch_decode(a)));
   } catch (...) {
     return KDA_ERR_HIP;
   }

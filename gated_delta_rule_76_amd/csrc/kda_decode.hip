@@ -21,11 +21,16 @@
 // touches whole contiguous state rows (fully coalesced 16-byte accesses).
 // The state for the thread's rows stays in registers between the reduction
 // and the write-back.
+#include "kda_check.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
+
+// Check sites of this unit (bits of the checked build's failure mask, before
+// the unit's shift).
+enum : int { kSiteState = 0, kSiteQKA = 1, kSiteV = 2, kSiteBeta = 3, kSiteOut = 4 };
 
 template <int DK, int DV>
 struct DecodeShape {
@@ -58,11 +63,13 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
   const int rg = tid / Sh::CG;
 
   float4* __restrict__ S4 = reinterpret_cast<float4*>(S + head * DK * DV);
+  // extents for the checked build (B * H = gridDim.x heads)
+  const long nhead = gridDim.x, ns4 = DK * DV / 4;
 
   // Issue the state loads first: they are the long-latency part.
   float4 s[Sh::RPT];
 #pragma unroll
-  for (int m = 0; m < Sh::RPT; ++m) s[m] = S4[(rg + Sh::RG * m) * Sh::CG + cg];
+  for (int m = 0; m < Sh::RPT; ++m) s[m] = S4[chk((rg + Sh::RG * m) * Sh::CG + cg, ns4, kSiteState)];
 
   __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
   // per-wave partial reductions, one float4 per column group (16-byte
@@ -71,20 +78,20 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
   __shared__ float red_kq[Sh::NW];
   // gate: one decay per channel, one per head (broadcast), or none; with the
   // fused prologue the gate and beta arrive as raw projections
-  float ah = gate == kGateHead ? load_scalar(alpha, head) : 1.f;
+  float ah = gate == kGateHead ? load_scalar(alpha, chk(head, nhead, kSiteQKA)) : 1.f;
   if (fused && gate == kGateHead) ah = gate_map(ah, gscale);
   for (int i = tid; i < DK; i += Sh::NTH) {
-    sq[i] = load_scalar(q, head * DK + i);
-    sk[i] = load_scalar(k, head * DK + i);
+    sq[i] = load_scalar(q, chk(head * DK + i, nhead * DK, kSiteQKA));
+    sk[i] = load_scalar(k, chk(head * DK + i, nhead * DK, kSiteQKA));
     float a = ah;
     if (gate == kGateChannel) {
-      a = load_scalar(alpha, head * DK + i);
+      a = load_scalar(alpha, chk(head * DK + i, nhead * DK, kSiteQKA));
       if (fused) a = gate_map(a, gscale);
     }
     sa[i] = a;
   }
-  for (int j = tid; j < DV; j += Sh::NTH) sv[j] = load_scalar(v, head * DV + j);
-  float bt = load_scalar(beta, head);
+  for (int j = tid; j < DV; j += Sh::NTH) sv[j] = load_scalar(v, chk(head * DV + j, nhead * DV, kSiteV));
+  float bt = load_scalar(beta, chk(head, nhead, kSiteBeta));
   if (fused) bt = sigmoid_f(bt);
   __syncthreads();
   if (fused) {  // L2-normalise q and k: wave 0 reduces, everyone rescales
@@ -146,7 +153,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
   if (rule == kRuleLinear) y0 = y1 = y2 = y3 = 0.f;  // no correction: u = beta v
   const float u0 = bt * (sv[4 * cg + 0] - y0), u1 = bt * (sv[4 * cg + 1] - y1);
   const float u2 = bt * (sv[4 * cg + 2] - y2), u3 = bt * (sv[4 * cg + 3] - y3);
-  if (rg == 0) {
+  if (rg == 0 && chk_ok(head * DV + 4 * cg, nhead * DV, kSiteOut, 4)) {
     const long ob = head * DV + 4 * cg;
     store_scalar(o, ob + 0, z0 + kq * u0);
     store_scalar(o, ob + 1, z1 + kq * u1);
@@ -158,7 +165,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NTH)) void decode_kernel(
     const int i = rg + Sh::RG * m;
     const float ki = sk[i];
     s[m].x += ki * u0; s[m].y += ki * u1; s[m].z += ki * u2; s[m].w += ki * u3;
-    S4[i * Sh::CG + cg] = s[m];
+    if (chk_ok(i * Sh::CG + cg, ns4, kSiteState)) S4[i * Sh::CG + cg] = s[m];
   }
 }
 
@@ -203,5 +210,7 @@ hipError_t dispatch_dk(const DecodeArgs& a) {
 hipError_t launch_decode(const DecodeArgs& a) {
   return a.bf16 ? dispatch_dk<Bf16>(a) : dispatch_dk<F32>(a);
 }
+
+unsigned decode_check_take() { return check_take(); }
 
 }  // namespace kda

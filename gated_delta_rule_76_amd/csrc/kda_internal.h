@@ -117,4 +117,18 @@ bool prefill_supported(bool bf16, int d_k, int d_v, int chunk);
 // every (batch, head): B * H * ceil(T / chunk) * slot bytes.
 bool prefill_slot_bytes(bool bf16, int d_k, int d_v, int chunk, size_t* slot);
 
+// Checked build (bounds checks in the kernels, see kda_check.h): each unit's
+// failed check sites on the current device since its last take (always 0 in
+// the normal build).
+unsigned prefill_check_take();
+unsigned decode_check_take();
+unsigned attnres_check_take();
+// A kernel whose one check fails on purpose, touching no memory (the checked
+// build's self-test; a no-op kernel in the normal build).
+hipError_t launch_check_probe(hipStream_t stream);
+// End of an entry point: in the checked build, synchronise `stream`, collect
+// every unit's failed sites and report any as KDA_ERR_CHECK (the mask is kept
+// for kda_check_sites); in the normal build, `status` unchanged.
+int checked_finish(hipStream_t stream, int status);
+
 }  // namespace kda

@@ -58,6 +58,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "kda_check.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -67,6 +68,22 @@ namespace {
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lvoid_t;
+
+// Check sites of this unit (bits of the checked build's failure mask).
+enum : int {
+  kSiteQK = 0,         // prep: q and k rows
+  kSiteAlpha = 1,      // prep: gate rows
+  kSiteBeta = 2,       // prep: beta
+  kSiteSlotStore = 3,  // prep: workspace slot stores
+  kSiteSlotLoad = 4,   // pass: slot copies into LDS
+  kSiteValue = 5,      // pass: value rows (copies and prefetch)
+  kSiteOut = 6,        // pass: output rows
+  kSiteS0 = 7,         // pass: initial state
+  kSiteST = 8,         // pass: final state
+  kSiteLds = 9,        // pass: LDS destinations of the direct loads
+  kSitePrefetch = 10,  // pass: slot prefetch
+  kSiteProbe = 11,     // the checked build's self-test
+};
 
 // ----------------------------------------------------------------- helpers
 // Batched LDS reads for the state chain: 16-byte reads at addr + offsets
@@ -335,11 +352,18 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   // holds chunk n of every chain in one contiguous run, which the state pass
   // reads at its step n.
   const int nchain = ntask / nchunk;
+  const long nrow = static_cast<long>(nchain) * T;  // token rows of every input tensor
   auto rowptr = [&](int task, int r) -> long {
     const int nl = task / nchain, chain = task - nl * nchain, n = n0 + nl;
     const int b = chain / H, h = chain - b * H;
     const int t = min(n * C + r, T - 1);
     return (static_cast<long>(b) * T + t) * H + h;
+  };
+
+  // a slot store of `bytes` at offset off of a task's slot
+  auto slot_ok = [&](const char* sl, long off, int bytes) {
+    return chk_ok((sl - ws) + off, static_cast<long>(ntask) * S::SLOT, kSiteSlotStore, bytes) &&
+           chk_ok(off, S::SLOT, kSiteSlotStore, bytes);
   };
 
   Raw8<St> ra[P::RPG], rk[P::RPG], rq[P::RPG];
@@ -351,16 +375,16 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         for (int rr = 0; rr < P::RPG; ++rr) {
           const long row = rowptr(task, rg * P::RPG + rr);
           if (gate == kGateChannel)
-            ra[rr].load(alpha + row * DK + ch0);
+            ra[rr].load(alpha + chk(row * DK + ch0, nrow * DK, kSiteAlpha, 8));
           else if (gate == kGateHead)
-            ra[rr].load_one(alpha + row);  // one decay for every channel of the head
+            ra[rr].load_one(alpha + chk(row, nrow, kSiteAlpha));  // one decay for every channel of the head
           else
             ra[rr].ones();
-          rk[rr].load(k + row * DK + ch0);
-          rq[rr].load(q + row * DK + ch0);
+          rk[rr].load(k + chk(row * DK + ch0, nrow * DK, kSiteQK, 8));
+          rq[rr].load(q + chk(row * DK + ch0, nrow * DK, kSiteQK, 8));
         }
       }
-      if (tid < C) rb = beta[rowptr(task, tid)];
+      if (tid < C) rb = beta[chk(rowptr(task, tid), nrow, kSiteBeta)];
     }
   };
   prefetch(blockIdx.x);
@@ -378,8 +402,9 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       uint32_t lo;
       asm volatile("v_lshlrev_b32 %0, %2, %1" : "=v"(lo) : "v"(lane), "i"(S::FB == 16 ? 4 : 5));
       for (int i = wave; i < S::NTRI; i += NW_PREP)
-        __builtin_nontemporal_store(*reinterpret_cast<const frag*>(sm.tm + i * S::FRAG + lo),
-                                    reinterpret_cast<frag*>(tm_slot + S::OFF_TM + i * S::FRAG + lo));
+        if (slot_ok(tm_slot, S::OFF_TM + i * S::FRAG + lo, S::FB))
+          __builtin_nontemporal_store(*reinterpret_cast<const frag*>(sm.tm + i * S::FRAG + lo),
+                                      reinterpret_cast<frag*>(tm_slot + S::OFF_TM + i * S::FRAG + lo));
     }
   };
 
@@ -555,7 +580,8 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
             half_acc[hh] = acc;
           }
           frag* dst = reinterpret_cast<frag*>(slot + S::OFF_PP + (S::tri(tr) + s2) * S::FRAG);
-          __builtin_nontemporal_store(M::from_acc(half_acc[0], half_acc[1]), &dst[lane]);
+          if (slot_ok(slot, S::OFF_PP + (S::tri(tr) + s2) * S::FRAG + lane * S::FB, S::FB))
+            __builtin_nontemporal_store(M::from_acc(half_acc[0], half_acc[1]), &dst[lane]);
         }
       // K+ and Q+ fragments: rows r, k = channels.
       constexpr int NKQ = 2 * S::NT * S::NKS;
@@ -565,7 +591,8 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         const lds_t* row = (w2 ? Qp : Kp) + (16 * t + c16) * P::LDK;
         const int kb = 32 * s2 + 4 * g;
         const frag f = (S::KODD && s2 == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
-        __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane]);
+        if (slot_ok(slot, (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG + lane * S::FB, S::FB))
+          __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane]);
       }
       // Kbar^T fragments: rows = channels 16t + c16, k = token rows, gathered
       // down a column of the row-major Kbar tile.
@@ -584,9 +611,11 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) f[4 + e] = colp[(r0 + 16 + e) * P::LDK];
         }
-        __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane]);
+        if (slot_ok(slot, S::OFF_KB + jj * S::FRAG + lane * S::FB, S::FB))
+          __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane]);
       }
-      if (tid < DK) reinterpret_cast<float*>(slot + S::OFF_GC)[tid] = sm.gC[tid];
+      if (tid < DK && slot_ok(slot, S::OFF_GC + 4 * tid, 4))
+        reinterpret_cast<float*>(slot + S::OFF_GC)[tid] = sm.gC[tid];
     }
     __syncthreads();  // the operand tiles are dead: Mf and Xf take their bytes
     // The next task's inputs load while this one finishes.  Issued after
@@ -692,7 +721,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
           }
           if constexpr (P::STAGE_TM)
             reinterpret_cast<frag*>(sm.tm + (S::tri(tr) + s2) * S::FRAG)[lane] = M::from8(t8);
-          else
+          else if (slot_ok(slot, S::OFF_TM + (S::tri(tr) + s2) * S::FRAG + lane * S::FB, S::FB))
             __builtin_nontemporal_store(M::from8(t8), &reinterpret_cast<frag*>(slot + S::OFF_TM + (S::tri(tr) + s2) * S::FRAG)[lane]);
         }
     }
@@ -793,21 +822,31 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   const int cw = wave - K::NCW;  // copy-wave index
   const long rs = static_cast<long>(H) * DV;  // element stride between tokens
   const long base = static_cast<long>(b) * T * rs + static_cast<long>(h) * DV + vb * DVB;
+  // extents for the checked build: this launch's slots (bytes), v and o
+  // (elements: B * H = gridDim.x chains), S0 and S_T (elements)
+  const long nslot = static_cast<long>(nchunk) * gridDim.x * K::SLOT;
+  const long nval = static_cast<long>(gridDim.x) * T * DV;
+  const long nstate = static_cast<long>(gridDim.x) * DK * DV;
+  constexpr int VE = 16 / K::ESZ;  // elements per 16-byte lane access
+  auto lds_ok = [&](long off) { return chk_ok(off, static_cast<long>(K::smem_bytes), kSiteLds, 1024); };
 
   // ------------------------------------------------------------ copy waves
   const int crow = lane / K::LPR, cbyte = 16 * (lane % K::LPR);
   auto stage_slot = [&](int n, int buf) {
-    const char* src = ws + (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
-    char* dst = lds + buf * K::SLOT;
-    for (int u = cw; u < K::SLOT / 1024; u += K::NCP)
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)(dst + u * 1024), 16, 0, 0);
+    const long s0 = (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
+    for (int u = cw; u < K::SLOT / 1024; u += K::NCP) {
+      const long off = chk(s0 + u * 1024 + lane * 16, nslot, kSiteSlotLoad, 16);
+      if (lds_ok(buf * K::SLOT + u * 1024))
+        __builtin_amdgcn_global_load_lds((gvoid_t*)(ws + off), (lvoid_t*)(lds + buf * K::SLOT + u * 1024), 16, 0, 0);
+    }
   };
   auto stage_v = [&](int n) {
-    char* dst = lds + K::OFF_V + (n & 1) * K::VTILE;
+    const int vo = K::OFF_V + (n & 1) * K::VTILE;
     for (int u = cw; u < K::NVI; u += K::NCP) {
       const int t = min((n0 + n) * C + u * K::RPI + crow, T - 1);  // rows past T: zeroed at use
-      const char* src = reinterpret_cast<const char*>(v + base + t * rs) + cbyte;
-      __builtin_amdgcn_global_load_lds((gvoid_t*)src, (lvoid_t*)(dst + u * 1024), 16, 0, 0);
+      const long e = chk(base + t * rs + cbyte / K::ESZ, nval, kSiteValue, VE);
+      if (lds_ok(vo + u * 1024))
+        __builtin_amdgcn_global_load_lds((gvoid_t*)(v + e), (lvoid_t*)(lds + vo + u * 1024), 16, 0, 0);
     }
   };
   // Prefetch wave: pulls its share of chunk n's slot (the value blocks of a
@@ -817,15 +856,17 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   // lands in a 1 KiB LDS sink that is never read.
   const int qu = (K::SLOT / 1024 + gridDim.y - 1) / gridDim.y;
   auto prefetch = [&](int n) {
-    const char* src = ws + (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
+    const long s0 = (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
     char* sink = lds + K::OFF_SINK;
     for (int i = 0; i < qu; ++i) {
       const int u = min(vb * qu + i, K::SLOT / 1024 - 1);
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(src + u * 1024 + lane * 16), (lvoid_t*)sink, 16, 0, 0);
+      const long off = chk(s0 + u * 1024 + lane * 16, nslot, kSitePrefetch, 16);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(ws + off), (lvoid_t*)sink, 16, 0, 0);
     }
     for (int u = 0; u < K::NVI; ++u) {
       const int t = min((n0 + n) * C + u * K::RPI + crow, T - 1);
-      __builtin_amdgcn_global_load_lds((gvoid_t*)(reinterpret_cast<const char*>(v + base + t * rs) + cbyte), (lvoid_t*)sink, 16, 0, 0);
+      const long e = chk(base + t * rs + cbyte / K::ESZ, nval, kSiteValue, VE);
+      __builtin_amdgcn_global_load_lds((gvoid_t*)(v + e), (lvoid_t*)sink, 16, 0, 0);
     }
   };
   // The compiler makes any LDS read wait for every earlier global access of
@@ -846,7 +887,8 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
     for (int u = 0; u < K::NVI; ++u) {
       const int r = u * K::RPI + crow, t = (n0 + n) * C + r;
-      if (r < C && t < T) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x[u];
+      if (r < C && t < T && chk_ok(base + t * rs + cbyte / K::ESZ, nval, kSiteOut, VE))
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(o + base + t * rs) + cbyte) = x[u];
     }
   };
 
@@ -875,11 +917,11 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     f32x4 Sa[S::NTK];
     frag sfr[S::NKS];  // bf16 (or fp32) operand copy of the state entering the chunk
     if (S0 != nullptr) {
-      const float* s0 = S0 + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+      const long s0 = (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
       for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Sa[ti][e] = s0[(16 * ti + e) * DV];
+        for (int e = 0; e < 4; ++e) Sa[ti][e] = S0[chk(s0 + (16 * ti + e) * DV, nstate, kSiteS0)];
     } else {
 #pragma unroll
       for (int ti = 0; ti < S::NTK; ++ti) Sa[ti] = z;
@@ -1015,11 +1057,12 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
     }
     if (nchunk > 0) __syncthreads();  // final [A]
     if (ST != nullptr) {
-      float* st = ST + (static_cast<long>(chain) * DK + 4 * g) * DV + col;
+      const long s0 = (static_cast<long>(chain) * DK + 4 * g) * DV + col;
 #pragma unroll
       for (int ti = 0; ti < S::NTK; ++ti)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[(16 * ti + e) * DV] = Sa[ti][e];
+        for (int e = 0; e < 4; ++e)
+          if (chk_ok(s0 + (16 * ti + e) * DV, nstate, kSiteST)) ST[s0 + (16 * ti + e) * DV] = Sa[ti][e];
     }
   } else if (outer) {
     // Output wave: O = Q+ S_in + P U into the output tile.
@@ -1373,5 +1416,20 @@ bool prefill_slot_bytes(bool bf16, int d_k, int d_v, int chunk, size_t* slot) {
   if (d_v != 16 && d_v != 32 && d_v != 64 && d_v != 128) return false;
   return (bf16 ? dispatch_dk<Bf16>(a, slot) : dispatch_dk<F32>(a, slot)) == hipSuccess;
 }
+
+namespace {
+// Self-test of the checked build: one check of an index one past the end of
+// a one-element extent; nothing is accessed.
+__global__ void check_probe_kernel(long n) {
+  if (threadIdx.x == 0) (void)chk(n, n, kSiteProbe);
+}
+}  // namespace
+
+hipError_t launch_check_probe(hipStream_t stream) {
+  hipLaunchKernelGGL(check_probe_kernel, dim3(1), dim3(64), 0, stream, 1L);
+  return hipGetLastError();
+}
+
+unsigned prefill_check_take() { return check_take(); }
 
 }  // namespace kda

@@ -54,7 +54,8 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment, bad dtype */
     KDA_ERR_UNSUPPORTED = 2, /* valid but not compiled: d_k, d_v, chunk combination */
     KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-    KDA_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+    KDA_ERR_HIP = 4,         /* the HIP runtime rejected a launch */
+    KDA_ERR_CHECK = 5        /* checked build only: a kernel index left its buffer (below) */
 } kda_status;
 
 /*
@@ -84,6 +85,30 @@ KDA_API int kda_version(void);
 
 /* Human-readable name of a kda_status value (static storage, never NULL). */
 KDA_API const char *kda_status_string(int status);
+
+/*
+ * Checked build.  libkda_checked.so is built from the same sources as
+ * libkda.so with bounds checks in every kernel: each index into a global
+ * buffer (inputs, outputs, states, the workspace) and each run-time LDS
+ * destination of a direct global-to-LDS load is compared with the extent of
+ * its buffer before the access.  An index outside it skips the access (a load
+ * reads element 0 of the same buffer instead, a store is dropped) and sets
+ * the bit of its check site.  Every entry point of the checked build then
+ * synchronises its stream and, if any site failed, returns KDA_ERR_CHECK;
+ * the outputs of that call are then unspecified.  It is a debugging build:
+ * calls are synchronous and slower, and results are otherwise those of
+ * libkda.so.  The normal build never returns KDA_ERR_CHECK.
+ *
+ * kda_build_checked returns 1 in the checked build, 0 in the normal one.
+ * kda_check_sites returns the site mask of the last call that returned
+ * KDA_ERR_CHECK in the process (0 if none): bits 0-15 prefill kernels
+ * (0 q/k rows, 1 gate, 2 beta, 3 workspace slot stores, 4 slot copies,
+ * 5 value rows, 6 output rows, 7 S0, 8 S_T, 9 LDS destinations, 10 slot
+ * prefetch, 11 self-test), bits 16-23 decode (16 state, 17 q/k/gate, 18 v,
+ * 19 beta, 20 output), bits 24-31 AttnRes (24 q, 25 k, 26 h, 27 out).
+ */
+KDA_API int kda_build_checked(void);
+KDA_API unsigned int kda_check_sites(void);
 
 /*
  * kda_fwd_chunked -- prefill: run the recurrence over T tokens for every

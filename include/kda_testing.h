@@ -47,6 +47,16 @@ KDA_API int kda_testing_wait_limit(void);
 KDA_API int kda_testing_set_ring_cap(size_t bytes);
 KDA_API size_t kda_testing_ring_cap(void);
 
+/*
+ * kda_testing_check_probe enqueues on `stream` a one-thread kernel that
+ * performs one bounds check meant to fail (an index one past the end of a
+ * one-element extent) and touches no memory.  In the checked build it
+ * returns KDA_ERR_CHECK with bit 11 set in kda_check_sites(); in the normal
+ * build the check compiles away and it returns KDA_OK.  KDA_ERR_HIP if the
+ * launch fails.
+ */
+KDA_API int kda_testing_check_probe(void *stream);
+
 #ifdef __cplusplus
 }
 #endif

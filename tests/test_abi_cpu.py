@@ -29,6 +29,21 @@ def test_library_exports_every_declared_symbol():
     assert sorted(kda.exported_symbols()) == _header_symbols()
 
 
+def test_checked_build_exports_the_same_abi():
+    """libkda_checked.so (bounds checks in the kernels) is built beside
+    libkda.so and exports every declared symbol; each reports which it is."""
+    assert os.path.exists(kda.CHECKED_LIB_PATH)
+    try:
+        assert kda.select_build(checked=True) == kda.CHECKED_LIB_PATH
+        assert sorted(kda.exported_symbols()) == _header_symbols()
+        assert kda.build_checked() is True
+        assert kda.check_sites() == 0
+    finally:
+        assert kda.select_build(checked=False) == kda.LIB_PATH
+    assert kda.build_checked() is False
+    assert kda.check_sites() == 0
+
+
 def test_version_and_status_strings():
     assert kda.version() == 1
     for code, name in kda.STATUS.items():

@@ -18,6 +18,9 @@ pytestmark = pytest.mark.gpu
     ("bf16", 64, 64, 128, 4096),
     ("bf16", 1024, 3, 128, 64),    # the largest L
     ("bf16", 61, 128, 100, 2048),  # d_k not a multiple of 64
+    ("bf16", 7, 9, 8, 8200),       # three sweeps of d, the last with one column group; one lane per key
+    ("f32", 3, 5, 512, 16),        # fewer than four layers; one layer per wave step in the scores
+    ("bf16", 4, 3, 256, 24),       # exactly one batch of four layers
 ])
 def test_attnres_parity(dtype, L, N, dk, d):
     import torch
