@@ -3,7 +3,8 @@
 Each .hip translation unit is compiled with hipcc in parallel, then linked
 into gated_delta_rule_76_amd/libkda.so; the same units compiled with
 -DKDA_CHECKED=1 (bounds checks in every kernel) are linked into
-libkda_checked.so, a debugging build.  The benchmark's calibration kernels
+libkda_checked.so, a debugging build; tests/c_abi_example, a plain-C caller of
+the ABI, is linked against libkda.so.  The benchmark's calibration kernels
 (csrc/calibrate.hip) go into a separate libkda_calibrate.so, outside the KDA
 C ABI.  Usage: python -m gated_delta_rule_76_amd.build
 """
@@ -66,6 +67,28 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi_example.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi_example")
+
+
+def _c_example() -> None:
+    """The plain-C caller of the ABI that the GPU tests run (gcc, C99, the HIP
+    runtime's C API; libkda.so found through an rpath relative to the binary)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C ABI example")
+    tmp = C_EXAMPLE + f".tmp{os.getpid()}"
+    cmd = [cc, "-O2", "-std=c99", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), C_EXAMPLE_SRC, "-o", tmp, "-L", PKG, "-lkda",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../gated_delta_rule_76_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C ABI example failed to build:\n{r.stderr}")
+    os.replace(tmp, C_EXAMPLE)
+
+
 def build(verbose: bool = True) -> str:
     """Build libkda.so, its bounds-checked twin libkda_checked.so (the same
     sources with -DKDA_CHECKED=1) and libkda_calibrate.so."""
@@ -78,8 +101,9 @@ def build(verbose: bool = True) -> str:
     _link(objs[:n], LIB)
     _link(objs[n:2 * n], CHECKED_LIB)
     _link(objs[2 * n:], CALIB_LIB)
+    _c_example()
     if verbose:
-        print(f"built {LIB}, {CHECKED_LIB} and {CALIB_LIB}")
+        print(f"built {LIB}, {CHECKED_LIB}, {CALIB_LIB} and {C_EXAMPLE}")
     return LIB
 
 
