@@ -134,6 +134,11 @@ SHAPES = [
     ("bf16", 128, 128, 64, 4, 130, 10),
     ("bf16", 64, 64, 32, 5, 99, 14),
     ("f32", 64, 64, 32, 5, 70, 14),
+    # more state-pass workgroups than CUs (128 chains x 4 value blocks): the
+    # workgroups run in several rounds and never wait on one another
+    ("bf16", 128, 128, 64, 8, 70, 16),
+    # one 16-column value block per chain (d_v = 16) with the bf16 prep
+    ("bf16", 128, 16, 64, 2, 150, 3),
 ]
 
 
