@@ -15,9 +15,12 @@
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates or frees device memory and keeps no state
- *     between calls beyond two process-wide caches: the device's CU count
- *     (read once) and, per kernel, whether it has already opted in to more
- *     than 64 KiB of LDS on a device (set once, thread-safely).
+ *     between calls beyond process-wide caches and settings: the device's
+ *     CU count (read once), per kernel whether it has already opted in to
+ *     more than 64 KiB of LDS on a device (set once, thread-safely), the
+ *     device address of kda_fwd_chunked_noalloc's array (looked up once per
+ *     device), the test settings of kda_testing.h, and in the checked build
+ *     the site mask of the last failed call.
  *   - Tensors are contiguous and row-major.  Pointers must be 16-byte aligned.
  *   - `dtype` selects the element type of q, k, v, alpha, beta and o:
  *     KDA_F32 (IEEE fp32) or KDA_BF16 (bfloat16).  The state is always fp32.
@@ -30,7 +33,8 @@
  *   - Every call returns a kda_status (0 = success).  No C++ exception ever
  *     crosses this boundary.
  *   - Results are deterministic: the same inputs, sizes and stream give
- *     bitwise identical outputs (no atomics, fixed reduction orders).
+ *     bitwise identical outputs (fixed reduction orders; no atomic ever
+ *     accumulates a value).
  */
 #ifndef KDA_H_
 #define KDA_H_
