@@ -11,6 +11,8 @@
 //   3. weighted sum: each thread owns two groups of 8 adjacent columns per
 //      sweep of d and walks the layers four at a time (eight 16-byte row
 //      loads in flight, streaming), accumulating in fp32
+// Global indices go through chk() / chk_ok() (kda_check.h): checked in the
+// checked build, free in the normal one.
 #include <math.h>
 #include <stdint.h>
 

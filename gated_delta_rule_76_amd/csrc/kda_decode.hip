@@ -20,7 +20,8 @@
 // value columns) for every RG-th key row, so each load instruction of a wave
 // touches whole contiguous state rows (fully coalesced 16-byte accesses).
 // The state for the thread's rows stays in registers between the reduction
-// and the write-back.
+// and the write-back.  Global indices go through chk() / chk_ok()
+// (kda_check.h): checked in the checked build, free in the normal one.
 #include "kda_check.h"
 #include "kda_device.h"
 #include "kda_internal.h"

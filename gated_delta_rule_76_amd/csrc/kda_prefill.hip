@@ -53,6 +53,10 @@
 // in this order, one 16-byte (bf16) or 32-byte (fp32) fragment per lane.
 // The reduction does not depend on which k each (lane, element) slot
 // carries as long as both operands agree.
+//
+// Bounds checks.  Every global index and run-time LDS destination below goes
+// through chk() / chk_ok() (kda_check.h): in the checked build a wrong index
+// is caught before the access; in the normal build they compile away.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
