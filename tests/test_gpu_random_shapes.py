@@ -1,9 +1,10 @@
-"""Seeded random sweep of prefill shapes and variants against the fp64
+"""Seeded random sweeps of prefill and decode shapes and variants against the fp64
 oracle: element type, key and value widths, chunk size, batch, heads,
 sequence length (ragged chunks and T below one chunk included), gate kind,
 update rule, with or without an initial state, and the segment-ring budget
-(default, or small enough to cut the sequence into several segments).  The
-draw is fixed (seed 2024), so every run checks the same 24 cases."""
+(default, or small enough to cut the sequence into several segments); and
+three decode steps per drawn decode shape and variant.  The draws are fixed
+(seeds 2024 and 4242), so every run checks the same 24 + 16 cases."""
 import numpy as np
 import pytest
 
@@ -64,3 +65,36 @@ def test_random_prefill_case(dtype, dk, dv, C, B, T, H, gate, rule, s0, small_ri
     eo, es = rel_err(to_np(o), o_ref), rel_err(to_np(st), s_ref)
     log(f"  rel_err o {eo:.2e}  S_T {es:.2e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def _decode_cases(n=16, seed=4242):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [(["f32", "bf16"][rng.integers(2)], int(rng.choice([16, 32, 64, 128])),
+             int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 5)), int(rng.integers(1, 6)),
+             ["channel", "head", "none"][rng.integers(3)], ["delta", "linear"][rng.integers(2)])
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,B,H,gate,rule", _decode_cases())
+def test_random_decode_case(dtype, dk, dv, B, H, gate, rule):
+    """Three consecutive decode steps on a random shape and variant (seed 4242)."""
+    import torch
+    import gated_delta_rule_76_amd as kda
+    from synth import decode_pool
+    log(f"[random decode] {dtype} dk{dk} dv{dv} B{B} H{H} {gate}/{rule}")
+    p = decode_pool(B, H, dk, dv, pool=3, dtype=dtype, gate_c=0.1, s0_std=0.05, seed=dk * 3 + dv + B * H)
+    S = torch.from_numpy(p["S"]).cuda()
+    Sref = p["S"].astype(np.float64)
+    for i in range(3):
+        a = {"channel": p["alpha"][i], "head": np.ascontiguousarray(p["alpha"][i][..., 0]),
+             "none": None}[gate]
+        dev = {n: to_dev(p[n][i], dtype) for n in ("q", "k", "v", "beta")}
+        o = kda.kda_decode_step(dev["q"], dev["k"], dev["v"], None if a is None else to_dev(a, dtype),
+                                dev["beta"], S, gate=gate, rule=rule)
+        o_ref, Sref = oracle.kda_decode_step(p["q"][i], p["k"][i], p["v"][i], a, p["beta"][i], Sref,
+                                             gate=gate, rule=rule)
+        torch.cuda.synchronize()
+        assert rel_err(to_np(o), o_ref) <= TOL[dtype], i
+    es = rel_err(S.cpu().numpy(), Sref)
+    log(f"  rel_err S {es:.2e}")
+    assert es <= TOL[dtype]
