@@ -12,7 +12,7 @@
  * state (section 3: the error-correcting write of a zero value), exactly.
  *
  * Built by the package's build step into tests/c_abi_example; run by
- * tests/test_gpu_c_abi.py.  Prints "c-abi example: ok" and exits 0 on
+ * tests/test_zy_c_abi.py.  Prints "c-abi example: ok" and exits 0 on
  * success; otherwise prints the first mismatch and exits 1.
  */
 #include <hip/hip_runtime_api.h>
