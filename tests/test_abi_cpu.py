@@ -248,3 +248,35 @@ def test_attnres_validation(kw, code):
     a.update(kw)
     assert kda.attnres_forward_raw(a["q"], a["k"], a["h"], a["out"], a["L"], a["N"], a["d_k"], a["d"],
                                    a["dtype"]) == code
+
+
+def test_workspace_query_properties():
+    """Seeded random sizes: while every chunk's slot fits the 512 MiB budget the
+    workspace is exactly one slot per (chain, chunk); past it, two ring
+    buffers plus one carried fp32 state per chain, never more than the budget
+    plus the carried states, and never less than two chunks' slots for every
+    chain (the ring always holds a segment in each half)."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(77))
+    cap = 512 << 20
+    for _ in range(300):
+        dtype = [kda.KDA_F32, kda.KDA_BF16][rng.integers(2)]
+        dk, dv = int(rng.choice([16, 32, 64, 128])), int(rng.choice([16, 32, 64, 128]))
+        C = int(rng.choice([16, 32, 64]))
+        B, H = int(rng.integers(1, 9)), int(rng.integers(1, 33))
+        T = int(rng.integers(0, 1 << 18))
+        slot = kda.workspace_bytes(1, C, 1, dk, dv, C, dtype)
+        got = kda.workspace_bytes(B, T, H, dk, dv, C, dtype)
+        if slot == 0:                       # combination not compiled
+            assert got == 0
+            continue
+        nchunk = -(-T // C)
+        chains = B * H
+        if nchunk == 0:
+            assert got == 0
+        elif chains * nchunk * slot <= cap:
+            assert got == chains * nchunk * slot
+        else:
+            state = chains * dk * dv * 4
+            assert got <= max(cap, 2 * chains * slot) + state
+            assert got >= 2 * chains * slot + state
