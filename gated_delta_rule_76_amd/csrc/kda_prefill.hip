@@ -212,6 +212,9 @@ struct Mma<Bf16> {
     return r;
   }
   static __device__ __forceinline__ void store8(lds_t* p, f32x8 x) { *reinterpret_cast<frag*>(p) = from8(x); }
+  static __device__ __forceinline__ void store4(lds_t* p, f32x4 x) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+  }
   static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -290,7 +293,58 @@ struct PrepCfg {
   static constexpr int NRG0 = NTH_PREP / NCG;
   static constexpr int NRG = NRG0 < C ? NRG0 : C;  // row groups in use
   static constexpr int RPG = C / NRG;               // rows per row group
-  static constexpr int LDK = DK + S::M::PAD;        // row stride of the C x DK tiles
+  // Operand-tile layout.  The bf16 tiles K+, K- and Q+ with d_k a multiple
+  // of 32 are kept in 16-byte chunks in matrix-core operand order: chunk
+  // 4s + g of row r holds channels 32s + 4g .. +3 and 32s + 16 + 4g .. +3,
+  // the eight values lane group g of a 16x16x32 product takes at k-step s,
+  // so every operand fragment is one 16-byte LDS read, and rows are padded
+  // by two chunks.  LDS serves 16-byte reads to 16 lanes at a time over 64
+  // banks (the lanes of one half wave whose lane / 4 has the same parity)
+  // and 8-byte writes to 16 consecutive lanes over 32 banks.  With this
+  // layout the fragment reads are free of bank conflicts, and so are the two
+  // 8-byte stores of each thread's eight channels when the threads holding
+  // channels 64 .. 127 store their upper four first (measured on gfx950: the
+  // row-major tile with 16-byte padding took 8 conflict cycles per pair
+  // read).  Kbar, read only down its columns, and the fp32 and d_k = 16
+  // tiles stay row-major with a padded row.
+  static constexpr bool SWZ = std::is_same<E, Bf16>::value && DK % 32 == 0;
+  static constexpr int LDK = SWZ ? DK + 16 : DK + S::M::PAD;  // row stride of K+, K-, Q+
+  static constexpr int LDB = DK + S::M::PAD;                  // row stride of Kbar
+  // element offset of (row r, channel c) in K+, K- or Q+
+  static constexpr __host__ __device__ int at(int r, int c) {
+    if constexpr (SWZ) {
+      const int u = c >> 2, j = u & 7;  // 4-channel unit, its place in the k-step
+      return r * LDK + 8 * (4 * (u >> 3) + (j & 3)) + 4 * (j >> 2) + (c & 3);
+    } else {
+      return r * LDK + c;
+    }
+  }
+  // element offset of the operand fragment of row r, k-step s, lane group g
+  static constexpr __host__ __device__ int frag_at(int r, int s, int g) { return r * LDK + 32 * s + 8 * g; }
+  // every (row, channel) has its own element of the C x LDK tile, and each
+  // fragment is the lane's channels in operand order
+  static constexpr bool layout_ok() {
+    if constexpr (!SWZ) {
+      return true;
+    } else {
+      bool used[C * LDK] = {};
+      for (int r = 0; r < C; ++r)
+        for (int c = 0; c < DK; ++c) {
+          const int o = at(r, c);
+          if (o < r * LDK || o >= r * LDK + DK || used[o]) return false;
+          used[o] = true;
+        }
+      for (int r = 0; r < C; ++r)
+        for (int s = 0; s < DK / 32; ++s)
+          for (int g = 0; g < 4; ++g)
+            for (int e = 0; e < 4; ++e)
+              if (frag_at(r, s, g) + e != at(r, 32 * s + 4 * g + e) ||
+                  frag_at(r, s, g) + 4 + e != at(r, 32 * s + 16 + 4 * g + e))
+                return false;
+      return true;
+    }
+  }
+  static_assert(layout_ok(), "operand-tile layout");
   static constexpr int LDF = C + 4;                 // fp32 C x C tiles (16-byte aligned rows)
   static constexpr int NPAIR = S::NT * (S::NT + 1) / 2;  // lower-triangular 16x16 tiles
   static constexpr int APW = (NPAIR + NW_PREP - 1) / NW_PREP;  // A tiles per wave
@@ -299,9 +353,10 @@ struct PrepCfg {
   // the end of the fragment stores.  The scan scratch is used before them,
   // Mf and Xf after them, so both reuse the same bytes.
   static constexpr int TILE = C * LDK * static_cast<int>(sizeof(lds_t));
+  static constexpr int TILEB = C * LDB * static_cast<int>(sizeof(lds_t));
   static constexpr int MF = C * LDF * 4;
   static constexpr int SCAN = NRG * DK * 4;
-  static constexpr int R_TILES = 4 * TILE;
+  static constexpr int R_TILES = 3 * TILE + TILEB;
   static constexpr int R_AFTER = 2 * MF;
   static constexpr int REGION = ((R_TILES > R_AFTER ? R_TILES : R_AFTER) > SCAN
                                      ? (R_TILES > R_AFTER ? R_TILES : R_AFTER)
@@ -349,6 +404,45 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
   const int cg = tid % P::NCG, rg = tid / P::NCG;
   const bool pro = rg < P::NRG;
   const int ch0 = 8 * cg;
+  // this thread's eight channels of row r of K+, K- or Q+: two 8-byte
+  // stores, the upper four channels first for channels 64 .. 127 (the order
+  // that keeps a row's stores free of bank conflicts)
+  const bool hi_first = P::SWZ && ((ch0 >> 6) & 1);
+  const int o_first = P::at(0, hi_first ? ch0 + 4 : ch0), o_second = P::at(0, hi_first ? ch0 : ch0 + 4);
+  // The per-thread fp32 scratch of eight channels (the decay scan, the
+  // chunk's decay) is stored and read as two 16-byte halves, in the order
+  // that keeps the accesses of a wave free of bank conflicts at d_k = 64, 128.
+  const bool hswap = ((cg >> 2) ^ (cg >> 3)) & 1;
+  auto put_halves = [&](float* p, f32x8 x) {
+    const f32x4 lo = __builtin_shufflevector(x, x, 0, 1, 2, 3), hi = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+    *reinterpret_cast<f32x4*>(p + (hswap ? 4 : 0)) = hswap ? hi : lo;
+    *reinterpret_cast<f32x4*>(p + (hswap ? 0 : 4)) = hswap ? lo : hi;
+  };
+  auto get_halves = [&](const float* p) -> f32x8 {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p + (hswap ? 4 : 0));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + (hswap ? 0 : 4));
+    return hswap ? __builtin_shufflevector(b, a, 0, 1, 2, 3, 4, 5, 6, 7)
+                 : __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto put8 = [&](lds_t* tile, int r, f32x8 x) {
+    if constexpr (P::SWZ) {
+      const f32x4 lo = __builtin_shufflevector(x, x, 0, 1, 2, 3), hi = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+      M::store4(&tile[r * P::LDK + o_first], hi_first ? hi : lo);
+      M::store4(&tile[r * P::LDK + o_second], hi_first ? lo : hi);
+    } else {
+      M::store8(&tile[r * P::LDK + ch0], x);
+    }
+  };
+  // this lane's operand fragment of row r, k-step s2 of K+, K- or Q+
+  auto opnd = [&](const lds_t* tile, int r, int s2) -> frag {
+    if constexpr (P::SWZ) {
+      return *reinterpret_cast<const frag*>(tile + P::frag_at(r, s2, g));
+    } else {
+      const lds_t* row = tile + r * P::LDK;
+      const int kb = 32 * s2 + 4 * g;
+      return (S::KODD && s2 == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
+    }
+  };
 
   // Token row of (task, r), clamped into the sequence so loads stay in bounds.
   // This launch covers chunks n0 .. n0 + nchunk - 1 of every chain.  Tasks
@@ -436,8 +530,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
         for (int e = 0; e < 8; ++e) run[e] *= ok ? a[e] : 1.f;
         lg[rr] = run;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) scan[rg * DK + ch0 + e] = run[e];
+      put_halves(&scan[rg * DK + ch0], run);
     }
     if (tid < C) {
       const float bx = load_scalar(&rb, 0);
@@ -474,12 +567,12 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
     __syncthreads();
     f32x8 pre, gc;
     if (pro) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { pre[e] = scan[rg * DK + ch0 + e]; gc[e] = sm.gC[ch0 + e]; }
+      pre = get_halves(&scan[rg * DK + ch0]);
+      gc = get_halves(&sm.gC[ch0]);
     }
     __syncthreads();  // the scan scratch is about to be overwritten by the tiles
 
-    // ---- 2. decay-scaled operand tiles, all row-major [r][channel]
+    // ---- 2. decay-scaled operand tiles [r][channel] (layout: PrepCfg)
     if (pro) {
 #pragma unroll
       for (int rr = 0; rr < P::RPG; ++rr) {
@@ -512,10 +605,10 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
           km[e] = kv * inv;
           kb[e] = km[e] * gc[e];
         }
-        M::store8(&Kp[r * P::LDK + ch0], kp);
-        M::store8(&Qp[r * P::LDK + ch0], qp);
-        M::store8(&Km[r * P::LDK + ch0], km);
-        M::store8(&Kb[r * P::LDK + ch0], kb);
+        put8(Kp, r, kp);
+        put8(Qp, r, qp);
+        put8(Km, r, km);
+        M::store8(&Kb[r * P::LDB + ch0], kb);
       }
     }
     __syncthreads();
@@ -535,15 +628,11 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
         for (int tc = 0; tc <= tr; ++tc, ++job) {
           if (job % NW_PREP != wave) continue;
-          const lds_t* arow = Kp + (16 * tr + c16) * P::LDK;
-          const lds_t* brow = Km + (16 * tc + c16) * P::LDK;
           frag af[S::NKS], bf[S::NKS];
 #pragma unroll
           for (int s2 = 0; s2 < S::NKS; ++s2) {
-            const int kb = 32 * s2 + 4 * g;
-            const bool h = S::KODD && s2 == S::NKS - 1;
-            af[s2] = h ? M::half(arow + kb) : M::pair(arow + kb, arow + kb + 16);
-            bf[s2] = h ? M::half(brow + kb) : M::pair(brow + kb, brow + kb + 16);
+            af[s2] = opnd(Kp, 16 * tr + c16, s2);
+            bf[s2] = opnd(Km, 16 * tc + c16, s2);
           }
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -559,21 +648,17 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
 #pragma unroll
         for (int s2 = 0; s2 <= tr / 2; ++s2, ++job) {
           if ((job + 1) % NW_PREP != wave) continue;
-          const lds_t* brow = Qp + (16 * tr + c16) * P::LDK;
           f32x4 half_acc[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int tc = 2 * s2 + hh;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (tc <= tr) {
-              const lds_t* arow = Km + (16 * tc + c16) * P::LDK;
               frag af[S::NKS], bf[S::NKS];
 #pragma unroll
               for (int ks = 0; ks < S::NKS; ++ks) {
-                const int kb = 32 * ks + 4 * g;
-                const bool h = S::KODD && ks == S::NKS - 1;
-                af[ks] = h ? M::half(arow + kb) : M::pair(arow + kb, arow + kb + 16);
-                bf[ks] = h ? M::half(brow + kb) : M::pair(brow + kb, brow + kb + 16);
+                af[ks] = opnd(Km, 16 * tc + c16, ks);
+                bf[ks] = opnd(Qp, 16 * tr + c16, ks);
               }
 #pragma unroll
               for (int ks = 0; ks < S::NKS; ++ks) acc = M::mma(af[ks], bf[ks], acc);
@@ -592,9 +677,7 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       for (int jj = wave; jj < NKQ; jj += NW_PREP) {
         const int w2 = jj & 1, ts = jj >> 1;  // ts = t * NKS + s
         const int t = ts / S::NKS, s2 = ts - t * S::NKS;
-        const lds_t* row = (w2 ? Qp : Kp) + (16 * t + c16) * P::LDK;
-        const int kb = 32 * s2 + 4 * g;
-        const frag f = (S::KODD && s2 == S::NKS - 1) ? M::half(row + kb) : M::pair(row + kb, row + kb + 16);
+        const frag f = opnd(w2 ? Qp : Kp, 16 * t + c16, s2);
         if (slot_ok(slot, (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG + lane * S::FB, S::FB))
           __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + (w2 ? S::OFF_QP : S::OFF_KP) + ts * S::FRAG)[lane]);
       }
@@ -603,17 +686,17 @@ __global__ __launch_bounds__(NTH_PREP, 2) void chunk_prep_kernel(
       constexpr int NKB = S::NTK * S::NCS;
       for (int jj = wave; jj < NKB; jj += NW_PREP) {
         const int t = jj / S::NCS, s2 = jj - t * S::NCS;
-        const lds_t* colp = Kb + 16 * t + c16;
+        const int col = 16 * t + c16;
         const int r0 = 32 * s2 + 4 * g;
         frag f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = colp[(r0 + e) * P::LDK];
+        for (int e = 0; e < 4; ++e) f[e] = Kb[(r0 + e) * P::LDB + col];
         if (S::CODD && s2 == S::NCS - 1) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) f[4 + e] = M::cvt(0.f);
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[4 + e] = colp[(r0 + 16 + e) * P::LDK];
+          for (int e = 0; e < 4; ++e) f[4 + e] = Kb[(r0 + 16 + e) * P::LDB + col];
         }
         if (slot_ok(slot, S::OFF_KB + jj * S::FRAG + lane * S::FB, S::FB))
           __builtin_nontemporal_store(f, &reinterpret_cast<frag*>(slot + S::OFF_KB + jj * S::FRAG)[lane]);
