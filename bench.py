@@ -245,7 +245,78 @@ def _calibration_lib():
     L.kda_calibrate_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.kda_calibrate_flops.restype = ctypes.c_double
     L.kda_calibrate_threads_per_block.restype = ctypes.c_int
+    L.kda_calibrate_lds.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    L.kda_calibrate_lds.restype = ctypes.c_int
     return L
+
+
+# LDS bank probe (kda_calibrate_lds): access forms, in the library's order.
+_LDS_FORMS = ["ds_read_b32", "ds_read_b64", "ds_read_b128", "ds_read2_b64", "ds_read2_b32",
+              "ds_write_b32", "ds_write_b64", "ds_write_b128", "ds_write2_b32"]
+_LDS_BASES = {2: (0, 4, 32, 36)}  # base lanes probed for each form (default: lane 0)
+_LDS_BLOCKS, _LDS_ITERS = 16, 256
+
+
+def _prep_store_offset(l: int, upper_first: bool) -> int:
+    """Byte offset of the first 8-byte tile store of lane l in the prep's
+    operand-order tile (d_k = 128: 288-byte rows, lane groups of 16 one row
+    each, row groups 4 rows apart): chunk 4s + (j & 3) of the row, half j >> 2,
+    for the thread's 4-channel unit u = 8s + j."""
+    r, cg = 4 * (l >> 4), l & 15
+    u = 2 * cg + (1 if upper_first and cg >= 8 else 0)
+    s, j = u >> 3, u & 7
+    return r * 288 + 2 * (8 * (4 * s + (j & 3)) + 4 * (j >> 2))
+
+
+def _lds_cases():
+    """The LDS probe list: (key, form, 64 byte offsets, -1 = inactive lane).
+    For each access form: a base lane j0 at byte 0 against every other lane k
+    at byte 256 (the same banks at 32 or 64 banks; a conflict means the LDS
+    serves the two lanes together), then lanes 0 and 1 at 128 bytes apart (a
+    conflict means the form spreads over 32 banks, none 64).  Then whole-wave
+    patterns of the prep's operand tiles."""
+    cases = []
+    for f in range(len(_LDS_FORMS)):
+        for j0 in _LDS_BASES.get(f, (0,)):
+            for k in range(64):
+                if k != j0:
+                    off = [-1] * 64
+                    off[j0], off[k] = 0, 256
+                    cases.append((("pair", f, j0, k), f, off))
+        off = [-1] * 64
+        off[0], off[1] = 0, 128
+        cases.append((("span", f), f, off))
+    pats = [
+        ("prep pair read, row-major tile, 272-byte rows (former layout)", 3,
+         [(l & 15) * 272 + 8 * (l >> 4) for l in range(64)]),
+        ("prep operand read, operand-order tile, 288-byte rows", 2,
+         [(l & 15) * 288 + 16 * (l >> 4) for l in range(64)]),
+        ("prep first tile store, both halves in channel order", 6,
+         [_prep_store_offset(l, False) for l in range(64)]),
+        ("prep first tile store, upper half first for channels 64-127", 6,
+         [_prep_store_offset(l, True) for l in range(64)]),
+    ]
+    for name, f, off in pats:
+        cases.append((("pattern", name), f, off))
+    return cases
+
+
+def run_lds_probes():
+    """Launch every LDS probe case once, in the order of _lds_cases()."""
+    import torch
+    L = _calibration_lib()
+    sink = torch.empty(_LDS_BLOCKS * 64, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    cases = _lds_cases()
+    for _, f, off in cases:
+        arr = (ctypes.c_int * 64)(*off)
+        rc = L.kda_calibrate_lds(f, arr, _LDS_BLOCKS, _LDS_ITERS, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"kda_calibrate_lds failed ({rc})")
+    torch.cuda.synchronize()
+    del sink
+    return len(cases)
 
 
 def bench_mfma_calibration(launches: int = 5, iters: int = 4000):
@@ -364,7 +435,8 @@ def cpu_baseline(x2, x3, decode_block, decode_sample_steps: int = 32):
 def profile_pass():
     """Fixed short run for rocprofv3 counter passes: a plain 1 GiB copy (the
     traffic calibration), the dense MFMA loops (the MFMA-busy calibration),
-    3 prefill launches, 3 decode launches, 3 AttnRes launches."""
+    the LDS bank probes, 3 prefill launches, 3 decode launches, 3 AttnRes
+    launches."""
     import torch
     n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written
     src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -377,6 +449,7 @@ def profile_pass():
     torch.cuda.empty_cache()
     cal = bench_mfma_calibration(launches=1, iters=2000)
     print(f"mfma loops: {cal['by_instruction_tflops']}", flush=True)
+    print(f"lds probes: {run_lds_probes()} launches", flush=True)
     bench_prefill(PREFILL, 3, 0)
     print("prefill: 3 launches", flush=True)
     bench_decode(3, 0)
@@ -472,11 +545,60 @@ def summarize(dirs):
             wr = tot[(lb, "WRITE_SIZE")] / _CALLS * 1024 / wcal
             out[lb] = {"hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
                        "hbm_bytes_per_launch": rd + wr}
+    _summarize_lds(dirs)
     for group, kv in out.items():
         print(f"[{group}]")
         for k, v in kv.items():
             print(f"{k}: {v:.6g}" if isinstance(v, float) and abs(v) < 100 else f"{k}: {v:.0f}")
     return out
+
+
+def _ranges(xs):
+    """[0, 1, 2, 5, 6] -> '0-2,5-6'"""
+    out, i = [], 0
+    while i < len(xs):
+        j = i
+        while j + 1 < len(xs) and xs[j + 1] == xs[j] + 1:
+            j += 1
+        out.append(f"{xs[i]}-{xs[j]}" if j > i else f"{xs[i]}")
+        i = j + 1
+    return ",".join(out)
+
+
+def _summarize_lds(dirs):
+    """The LDS bank model from the lds_probe dispatches of a profile pass
+    with SQ_LDS_BANK_CONFLICT: dispatches in launch order are the cases of
+    _lds_cases(); conflict cycles are per wave access."""
+    import glob
+    per = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            for r in csv.DictReader(open(f)):
+                if "lds_probe" in r["Kernel_Name"] and r["Counter_Name"] == "SQ_LDS_BANK_CONFLICT":
+                    k = int(r["Dispatch_Id"])
+                    per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    if not per:
+        return
+    cases = _lds_cases()
+    vals = [per[k] / (_LDS_BLOCKS * _LDS_ITERS) for k in sorted(per)]
+    if len(vals) != len(cases):
+        print(f"# lds_probe: {len(vals)} dispatches, expected {len(cases)}; not summarised")
+        return
+    res = {key: v for (key, _, _), v in zip(cases, vals)}
+    print(f"# LDS bank model (lds_probe, {len(vals)} dispatches of {_LDS_BLOCKS} one-wave workgroups x "
+          f"{_LDS_ITERS} accesses; two active lanes, the base lane j0 at byte 0 and lane k at byte 256):")
+    print("#   access form     | lanes served together with the base lane          | banks (4 bytes)")
+    for f, name in enumerate(_LDS_FORMS):
+        groups = []
+        for j0 in _LDS_BASES.get(f, (0,)):
+            same = sorted([j0] + [k for k in range(64) if k != j0 and res[("pair", f, j0, k)] > 0.5])
+            groups.append(f"j0={j0}: {_ranges(same)}")
+        banks = 32 if res[("span", f)] > 0.5 else 64
+        print(f"#   {name:15s} | {'; '.join(groups):49s} | {banks}")
+    print("# whole-wave patterns, conflict cycles per access:")
+    for (key, _, _), v in zip(cases, vals):
+        if key[0] == "pattern":
+            print(f"#   {key[1]}: {v:.2f}")
 
 
 # Phases of a default run, in order: (label, kernels of one call).  A prefill

@@ -111,3 +111,50 @@ def test_trace_summary(tmp_path):
     assert "| prefill_b4_h16_t16k | 2 | 767.0 |" in text
     assert "| prefill_h16_t128k | 1 |" in text
     assert "| prefill_b4_h16_t16k (per-head gate) | 1 |" in text
+
+
+def test_lds_probe_cases_stay_in_bounds():
+    """Every LDS probe case is accepted by kda_calibrate_lds: offsets below
+    65216 bytes, aligned to the access width, two active lanes per pair case."""
+    width = [4, 8, 16, 8, 4, 4, 8, 16, 4]
+    cases = bench._lds_cases()
+    assert len(cases) == 9 * 63 + 3 * 63 + 9 + 4
+    for key, form, off in cases:
+        assert len(off) == 64
+        act = [o for o in off if o >= 0]
+        assert all(o < 65216 and o % width[form] == 0 for o in act), key
+        if key[0] in ("pair", "span"):
+            assert len(act) == 2, key
+        else:
+            assert len(act) == 64, key
+
+
+def test_lds_probe_summary(tmp_path):
+    """The LDS model table from probe dispatches: a toy ground truth (lanes
+    served together in groups of 16 for odd forms and 32 for even forms;
+    32 banks for forms 0-4, 64 for 5-8) comes back out of the summary."""
+    cases = bench._lds_cases()
+    per_access = bench._LDS_BLOCKS * bench._LDS_ITERS
+    rows = []
+    for key, form, off in cases:
+        if key[0] == "pair":
+            _, f, j0, k = key
+            grp = 16 if f % 2 else 32
+            v = 1.0 if j0 // grp == k // grp else 0.0
+        elif key[0] == "span":
+            v = 1.0 if key[1] < 5 else 0.0
+        else:
+            v = 3.0
+        rows.append((f"void (anonymous namespace)::lds_probe<{form}>(...)", 16, "SQ_LDS_BANK_CONFLICT",
+                     v * per_access))
+    _write_counters(str(tmp_path / "sq"), rows)
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        bench._summarize_lds([str(tmp_path / "sq")])
+    text = buf.getvalue()
+    assert "ds_read_b32     | j0=0: 0-31" in text
+    assert "ds_read_b64     | j0=0: 0-15" in text
+    assert "ds_read_b128    | j0=0: 0-31; j0=4: 0-31; j0=32: 32-63; j0=36: 32-63" in text
+    lines = {ln.split("|")[0].strip("# ").strip(): ln.split("|")[2].strip() for ln in text.splitlines() if "|" in ln}
+    assert lines["ds_read_b32"] == "32" and lines["ds_write_b32"] == "64"
+    assert text.count(": 3.00") == 4
