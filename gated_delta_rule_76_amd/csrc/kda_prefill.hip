@@ -846,6 +846,18 @@ struct PassCfg {
   static constexpr int RPI = 64 / LPR;                   // rows per wave instruction
   static constexpr int NVI = (C + RPI - 1) / RPI;        // instructions per tile
   static constexpr int VTILE = NVI * 1024;               // bytes per tile buffer
+  // With two slabs, rows with bit 2 set swap their two slab halves in LDS:
+  // (row r, 16-byte piece k) sits at 16-byte position r * LPR + (k ^ VSW)
+  // for those rows, r * LPR + k otherwise.  The compute waves read values and
+  // write outputs down columns, lane groups four rows apart; without the swap
+  // those rows share LDS banks (one extra cycle per half wave).  For a wave,
+  // the swap is the same for every row it touches, so its addresses keep one
+  // base.  One-slab tiles are left as they are.
+  static constexpr int VSW = NSLAB == 2 ? LPR / 2 : 0;
+  static_assert(RPI % 8 == 0, "the swap keeps rows in their 1 KiB copy unit");
+  static constexpr __host__ __device__ int vidx(int r, int c) {  // element index of (row r, column c)
+    return ((r * LPR + (((c * ESZ) / 16) ^ (VSW * ((r >> 2) & 1)))) * 16 + (c * ESZ) % 16) / ESZ;
+  }
   static_assert(VROW % 16 == 0 && 64 % LPR == 0 && NSLAB <= 2, "pass map");
   // Hand-over areas: the state operand S (NKS fragments per slab, double
   // buffered: written at the end of chunk n for chunk n + 1), U (NCS
@@ -918,7 +930,8 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
   auto lds_ok = [&](long off) { return chk_ok(off, static_cast<long>(K::smem_bytes), kSiteLds, 1024); };
 
   // ------------------------------------------------------------ copy waves
-  const int crow = lane / K::LPR, cbyte = 16 * (lane % K::LPR);
+  // the tile row and 16-byte piece this lane moves (position lane of a copy unit)
+  const int crow = lane / K::LPR, cbyte = 16 * ((lane % K::LPR) ^ (K::VSW * ((crow >> 2) & 1)));
   auto stage_slot = [&](int n, int buf) {
     const long s0 = (static_cast<long>(n) * gridDim.x + chain) * K::SLOT;
     for (int u = cw; u < K::SLOT / 1024; u += K::NCP) {
@@ -1085,7 +1098,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16);
+        for (int e = 0; e < 4; ++e) vr[tr][e] = load_scalar(vt, K::vidx(16 * tr + 4 * g + e, 16 * slab + c16));
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
@@ -1204,7 +1217,7 @@ __attribute__((amdgpu_waves_per_eu(PassCfg<E, DK, DVB, C>::WPE, PassCfg<E, DK, D
 #pragma unroll
       for (int tr = 0; tr < S::NT; ++tr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_scalar(ot, (16 * tr + 4 * g + e) * DVB + 16 * slab + c16, O[tr][e]);
+        for (int e = 0; e < 4; ++e) store_scalar(ot, K::vidx(16 * tr + 4 * g + e, 16 * slab + c16), O[tr][e]);
       if (K::NBUF == 1) __syncthreads();  // [B]
     }
     if (nchunk > 0) __syncthreads();  // final [A]
