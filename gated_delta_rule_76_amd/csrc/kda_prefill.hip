@@ -299,14 +299,15 @@ struct PrepCfg {
   // the eight values lane group g of a 16x16x32 product takes at k-step s,
   // so every operand fragment is one 16-byte LDS read, and rows are padded
   // by two chunks.  LDS serves 16-byte reads to 16 lanes at a time over 64
-  // banks (the lanes of one half wave whose lane / 4 has the same parity)
-  // and 8-byte writes to 16 consecutive lanes over 32 banks.  With this
-  // layout the fragment reads are free of bank conflicts, and so are the two
-  // 8-byte stores of each thread's eight channels when the threads holding
-  // channels 64 .. 127 store their upper four first (measured on gfx950: the
-  // row-major tile with 16-byte padding took 8 conflict cycles per pair
-  // read).  Kbar, read only down its columns, and the fp32 and d_k = 16
-  // tiles stay row-major with a padded row.
+  // banks (within a half wave, the lanes whose lane / 4 has an even, or an
+  // odd, number of set bits) and 8-byte writes to 16 consecutive lanes over
+  // 32 banks.  With this layout the fragment reads are free of bank
+  // conflicts, and so are the two 8-byte stores of each thread's eight
+  // channels when the threads holding channels 64 .. 127 store their upper
+  // four first (measured on gfx950: the row-major tile with 16-byte padding
+  // took 8 conflict cycles per pair read).  Kbar, read only down its
+  // columns, and the fp32 and d_k = 16 tiles stay row-major with a padded
+  // row.
   static constexpr bool SWZ = std::is_same<E, Bf16>::value && DK % 32 == 0;
   static constexpr int LDK = SWZ ? DK + 16 : DK + S::M::PAD;  // row stride of K+, K-, Q+
   static constexpr int LDB = DK + S::M::PAD;                  // row stride of Kbar
